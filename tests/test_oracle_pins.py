@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test fixes the oracle to something outside itself: a value the pages
+print (tests/golden), a closed form, a library routine (torch's
+scaled_dot_product_attention in float64), an exact construction with a
+known answer, or an independent per-token brute force written with Python
+loops. ``test_planted_mistakes`` then plants plausible mistakes in copies of
+oracle functions and shows that these pins catch each one.
+"""
+import collections
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import vsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------
+# geometry
+# ----------------------------------------------------------------------------
+
+def test_wan_routing_log_line():
+    g = _golden("wan_routing_log.json")
+    geo = O.geometry(g["dit_seq_shape"], g["block_size"])
+    s = O.routing_summary(geo, g["topk"])
+    assert s["seq_len"] == g["seq_len"]
+    assert s["num_blocks"] == g["num_blocks"]
+    assert s["keep_ratio"] == g["keep_ratio"]
+    assert list(s["dit_seq_shape"]) == g["dit_seq_shape"]
+    assert geo.cube_volume == _golden("block_shapes.json")["wan_block_tokens"]
+
+
+def test_fastbsa_sparsity_keeps_one_sixteenth():
+    g = _golden("block_shapes.json")
+    geo = O.geometry((16, 46, 80), g["fastbsa_chunk"])
+    assert geo.cube_volume == g["h3_block_tokens"]
+    keep = geo.num_blocks * (1.0 - g["fastbsa_sparsity"])
+    assert keep == 60.0 and geo.num_blocks == 960
+
+
+@pytest.mark.parametrize("latent,cube,prefix", [
+    ((31, 22, 40), (4, 8, 8), 0), ((16, 46, 80), (4, 4, 4), 0),
+    ((21, 30, 52), (4, 4, 4), 512), ((5, 6, 7), (2, 4, 4), 0),
+    ((3, 5, 7), (4, 8, 8), 0), ((4, 4, 4), (2, 2, 2), 20), ((1, 1, 1), (1, 1, 1), 0),
+])
+def test_block_counts_closed_form(latent, cube, prefix):
+    geo = O.geometry(latent, cube, prefix)
+    V = int(np.prod(cube))
+    counts = geo.counts
+    assert counts.sum() == geo.seq_len == prefix + int(np.prod(latent))
+    # prefix blocks: V tokens each, the last one holds the remainder
+    for p in range(geo.num_prefix_blocks):
+        assert counts[p] == min(V, prefix - p * V)
+    # video cubes: product over axes of min(cube, grid - start)
+    nT, nH, nW = geo.nblk
+    for bt in range(nT):
+        for bh in range(nH):
+            for bw in range(nW):
+                c = geo.num_prefix_blocks + (bt * nH + bh) * nW + bw
+                want = 1
+                for L, cs, b in zip(latent, cube, (bt, bh, bw)):
+                    want *= min(cs, L - b * cs)
+                assert counts[c] == want
+
+
+def test_valid_count_histograms():
+    h = lambda g, lo: dict(collections.Counter(g.counts[lo:].tolist()))
+    assert h(O.geometry((31, 22, 40), (4, 8, 8)), 0) == {256: 70, 192: 45, 144: 5}
+    assert h(O.geometry((16, 46, 80), (4, 4, 4)), 0) == {64: 880, 32: 80}
+    g5 = O.geometry((21, 30, 52), (4, 4, 4), 512)
+    assert (g5.num_blocks, g5.num_prefix_blocks) == (624, 8)
+    assert h(g5, 8) == {64: 455, 32: 65, 16: 91, 8: 13}
+
+
+def test_block_map_by_enumeration():
+    """Every token is in exactly one block; membership matches a direct walk
+    over the cube grid."""
+    latent, cube, P = (5, 6, 7), (2, 4, 4), 11
+    geo = O.geometry(latent, cube, P)
+    T, H, W = latent
+    seen = np.zeros(geo.seq_len, dtype=int)
+    for m in geo.members:
+        seen[m] += 1
+    assert np.all(seen == 1)
+    c = 0
+    for bt in range(0, T, cube[0]):
+        for bh in range(0, H, cube[1]):
+            for bw in range(0, W, cube[2]):
+                toks = sorted(P + (t * H + hh) * W + w
+                              for t in range(bt, min(T, bt + cube[0]))
+                              for hh in range(bh, min(H, bh + cube[1]))
+                              for w in range(bw, min(W, bw + cube[2])))
+                assert list(geo.members[geo.num_prefix_blocks + c]) == toks
+                c += 1
+    assert c == geo.num_blocks
+
+
+# ----------------------------------------------------------------------------
+# pool
+# ----------------------------------------------------------------------------
+
+def _coord_features(latent, prefix, D=8):
+    T, H, W = latent
+    x = np.zeros((prefix + T * H * W, D))
+    x[:prefix, 3] = np.arange(prefix)
+    t, hh, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    x[prefix:, 0] = t.ravel()
+    x[prefix:, 1] = hh.ravel()
+    x[prefix:, 2] = w.ravel()
+    return x
+
+
+@pytest.mark.parametrize("latent,cube,prefix", [
+    ((31, 22, 40), (4, 8, 8), 0), ((21, 30, 52), (4, 4, 4), 512), ((5, 6, 7), (2, 4, 4), 20),
+])
+def test_pool_centroid(latent, cube, prefix):
+    """Pooling the coordinates gives the centroid of each block's valid
+    region: the midpoint of each clipped axis range."""
+    geo = O.geometry(latent, cube, prefix)
+    pooled = O.pool(_coord_features(latent, prefix), geo)
+    V = geo.cube_volume
+    for p in range(geo.num_prefix_blocks):
+        lo, hi = p * V, min(prefix, (p + 1) * V) - 1
+        assert pooled[p, 3] == pytest.approx((lo + hi) / 2, abs=1e-12)
+    nT, nH, nW = geo.nblk
+    for bt in range(nT):
+        for bh in range(nH):
+            for bw in range(nW):
+                c = geo.num_prefix_blocks + (bt * nH + bh) * nW + bw
+                for a, b in enumerate((bt, bh, bw)):
+                    lo = b * cube[a]
+                    hi = min(latent[a], lo + cube[a]) - 1
+                    assert pooled[c, a] == pytest.approx((lo + hi) / 2, abs=1e-12)
+
+
+def test_pool_centroid_wan_last_cube_by_hand():
+    geo = O.geometry((31, 22, 40), (4, 8, 8))
+    pooled = O.pool(_coord_features((31, 22, 40), 0), geo)
+    # last cube: t in 28..30, h in 16..21, w in 32..39
+    assert tuple(pooled[-1, :3]) == (29.0, 18.5, 35.5)
+
+
+def test_pool_constant_and_linear():
+    geo = O.geometry((5, 6, 7), (2, 4, 4), 9)
+    x = np.full((geo.seq_len, 4), 3.25)
+    assert np.all(O.pool(x, geo) == 3.25)
+    y = _rand((geo.seq_len, 4), 0)
+    np.testing.assert_allclose(O.pool(2 * x - y, geo), 2 * O.pool(x, geo) - O.pool(y, geo),
+                               atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# score + select
+# ----------------------------------------------------------------------------
+
+def test_select_known_order_construction():
+    """q = e0 everywhere and k = r_cube * e0: cube scores are r_j / sqrt(D),
+    so the kept set is the topk largest r."""
+    latent, cube, D = (5, 6, 7), (2, 4, 4), 16
+    geo = O.geometry(latent, cube)
+    r = np.random.default_rng(3).permutation(geo.num_blocks).astype(float) - 4.0
+    q = np.zeros((geo.seq_len, D)); q[:, 0] = 1.0
+    k = np.zeros((geo.seq_len, D)); k[:, 0] = r[geo.block_of_token]
+    s = O.block_scores(O.pool(q, geo), O.pool(k, geo, video_only=True), D)
+    np.testing.assert_allclose(s, np.broadcast_to(r / 4.0, s.shape), atol=1e-14)
+    for topk in (1, 3, geo.num_blocks):
+        sel = O.select_topk(s, topk)
+        want = np.sort(np.argsort(-r)[:topk])
+        assert np.all(sel == want)
+
+
+def test_select_matches_full_sort():
+    s = _rand((7, 50), 11)
+    for topk in (1, 5, 49, 50):
+        sel = O.select_topk(s, topk)
+        for i in range(7):
+            want = sorted(sorted(range(50), key=lambda j: (-s[i, j], j))[:topk])
+            assert list(sel[i]) == want
+
+
+def test_select_ties_go_to_lower_index():
+    s = np.array([[1.0, 2.0, 2.0, 0.5, 2.0, 2.0]])
+    assert list(O.select_topk(s, 2)[0]) == [1, 2]
+    assert list(O.select_topk(s, 3)[0]) == [1, 2, 4]
+    assert list(O.select_topk(np.zeros((1, 5)), 2)[0]) == [0, 1]
+
+
+@pytest.mark.parametrize("topk", [0, -1, 13])
+def test_select_rejects_bad_topk(topk):
+    with pytest.raises(ValueError):
+        O.select_topk(np.zeros((2, 12)), topk)
+
+
+def test_check_selection_band():
+    s = np.array([[0.5, 0.3, 0.3 + 5e-7, 0.1]])
+    ok = O.check_selection(np.array([[0, 1]]), s, 2)
+    assert ok["mismatch_rows"] == [] and ok["band_rows"] == 1
+    ok2 = O.check_selection(np.array([[0, 2]]), s, 2)
+    assert ok2["mismatch_rows"] == []
+    bad = O.check_selection(np.array([[1, 2]]), s, 2)
+    assert bad["mismatch_rows"] == [0]
+    assert O.check_selection(np.array([[2, 0]]), s, 2)["mismatch_rows"] == [0]
+
+
+# ----------------------------------------------------------------------------
+# attend
+# ----------------------------------------------------------------------------
+
+def _sdpa64(q, k, v):
+    import torch
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0].numpy()
+
+
+@pytest.mark.parametrize("latent,cube,prefix,D", [
+    ((8, 8, 8), (4, 4, 4), 0, 64), ((5, 6, 7), (2, 4, 4), 0, 32),
+    ((3, 5, 7), (4, 8, 8), 0, 16), ((4, 4, 4), (2, 2, 2), 20, 16),
+])
+def test_all_blocks_equals_dense_sdpa(latent, cube, prefix, D):
+    geo = O.geometry(latent, cube, prefix)
+    q, k, v = (_rand((geo.seq_len, D), s) for s in (1, 2, 3))
+    _, sel, out = O.forward_head(q, k, v, geo, geo.num_blocks)
+    np.testing.assert_allclose(out, _sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one_and_convex_hull():
+    geo = O.geometry((5, 6, 7), (2, 4, 4), 9)
+    D = 16
+    q, k, v = (_rand((geo.seq_len, D), s) for s in (4, 5, 6))
+    s = O.block_scores(O.pool(q, geo), O.pool(k, geo, video_only=True), D)
+    sel = O.select_topk(s, 3)
+    out, rs = O.attend_dense_masked(q, k, v, sel, geo, return_rowsums=True)
+    assert np.max(np.abs(rs - 1.0)) < 1e-12
+    for i in range(geo.num_q_blocks):
+        keep = np.isin(geo.block_of_token, O.kept_blocks(sel[i], geo))
+        rows = geo.members[i]
+        assert np.all(out[rows] <= v[keep].max(0) + 1e-12)
+        assert np.all(out[rows] >= v[keep].min(0) - 1e-12)
+    ones = O.attend_dense_masked(q, k, np.ones_like(v), sel, geo)
+    assert np.max(np.abs(ones - 1.0)) < 1e-12
+    scaled = O.attend_dense_masked(q, k, -2.5 * v, sel, geo)
+    np.testing.assert_allclose(scaled, -2.5 * out, rtol=0, atol=1e-12)
+
+
+def test_equal_keys_give_mean_of_kept_values():
+    geo = O.geometry((5, 6, 7), (2, 4, 4), 5)
+    D = 8
+    q = _rand((geo.seq_len, D), 1)
+    k = np.tile(_rand((1, D), 2), (geo.seq_len, 1))
+    v = _rand((geo.seq_len, D), 3)
+    sel = O.select_topk(_rand((geo.num_q_blocks, geo.num_blocks), 4), 4)
+    out = O.attend_dense_masked(q, k, v, sel, geo)
+    for i in range(geo.num_q_blocks):
+        keep = np.isin(geo.block_of_token, O.kept_blocks(sel[i], geo))
+        np.testing.assert_allclose(out[geo.members[i]],
+                                   np.broadcast_to(v[keep].mean(0), (geo.members[i].size, D)),
+                                   atol=1e-12)
+
+
+BRUTE_CASES = [
+    ((8, 8, 8), (4, 4, 4), 0, 4, 16),      # the tiny workload's grid
+    ((5, 6, 7), (2, 4, 4), 0, 5, 8),       # partial cubes on every axis
+    ((3, 5, 7), (4, 8, 8), 0, 1, 8),       # one cube larger than the grid
+    ((4, 4, 4), (2, 2, 2), 20, 3, 8),      # prefix with a partial prefix block
+]
+
+
+@pytest.mark.parametrize("latent,cube,prefix,topk,D", BRUTE_CASES)
+def test_brute_force_per_token(latent, cube, prefix, topk, D):
+    geo = O.geometry(latent, cube, prefix)
+    q, k, v = (_rand((geo.seq_len, D), s) for s in (7, 8, 9))
+    _, _, out = O.forward_head(q, k, v, geo, topk)
+    ql, kl, vl = q.tolist(), k.tolist(), v.tolist()
+    toks = np.random.default_rng(0).choice(geo.seq_len, size=min(12, geo.seq_len), replace=False)
+    toks = sorted(set(toks.tolist()) | {0, geo.seq_len - 1})
+    for n in toks:
+        bf = O.brute_force_token(ql, kl, vl, latent, cube, prefix, topk, n)
+        np.testing.assert_allclose(out[n], bf, rtol=0, atol=1e-12)
+
+
+def test_shift_of_all_keys_changes_nothing():
+    """Adding one vector b to every key adds q.b to a whole row of logits and
+    qbar_i.b to a whole row of block scores: selection and output stay."""
+    geo = O.geometry((5, 6, 7), (2, 4, 4), 7)
+    D = 16
+    q, k, v = (_rand((geo.seq_len, D), s) for s in (1, 2, 3))
+    b = 3.0 * _rand((1, D), 4)
+    s1, sel1, o1 = O.forward_head(q, k, v, geo, 4)
+    s2, sel2, o2 = O.forward_head(q, k + b, v, geo, 4)
+    assert np.all(sel1 == sel2)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(s2 - s1, np.broadcast_to((O.pool(q, geo) @ b.T) / 4.0, s1.shape),
+                               atol=1e-12)
+
+
+def test_decode_bf16_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4049, 0x7F7F, 0x0001], dtype=np.uint16)
+    want = [1.0, -1.0, 0.0, -0.0, 3.140625, 3.3895313892515355e38, 2.0 ** -133]
+    assert O.decode_bf16(bits).tolist() == want
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each must be caught by one of the pins above
+# ----------------------------------------------------------------------------
+
+def _pool_zero_padded(x, g, video_only=False):
+    first = g.num_prefix_blocks if video_only else 0
+    out = np.empty(x.shape[:-2] + (g.num_q_blocks - first, x.shape[-1]))
+    for i in range(first, g.num_q_blocks):
+        out[..., i - first, :] = x[..., g.members[i], :].sum(axis=-2) / g.cube_volume
+    return out
+
+
+def _select_ties_high(scores, topk):
+    order = np.argsort(-scores[..., ::-1], axis=-1, kind="stable")[..., :topk]
+    return np.sort(scores.shape[-1] - 1 - order, axis=-1)
+
+
+def _kept_no_prefix(sel_row, g):
+    return np.array([g.num_prefix_blocks + int(j) for j in sel_row])
+
+
+def _scores_swapped(qbar, kbar, D):
+    # operands swapped: s[i, j] = kbar_i . qbar_j (square when nq == nb)
+    return np.swapaxes(np.matmul(qbar, np.swapaxes(kbar, -1, -2)), -1, -2) * D ** -0.5
+
+
+def _attend_wrong_scale(q, k, v, sel, g, query_blocks=None, return_rowsums=False):
+    # logits left unscaled (the head_dim ** -0.5 factor dropped)
+    return O.__dict__["_orig_attend"](q * math.sqrt(q.shape[1]), k, v, sel, g,
+                                      query_blocks, return_rowsums)
+
+
+@pytest.mark.parametrize("target,mutant,pin", [
+    ("pool", _pool_zero_padded, "centroid"),
+    ("select_topk", _select_ties_high, "ties"),
+    ("kept_blocks", _kept_no_prefix, "brute_prefix"),
+    ("block_scores", _scores_swapped, "brute_padded"),
+    ("attend_dense_masked", _attend_wrong_scale, "sdpa"),
+])
+def test_planted_mistakes(monkeypatch, target, mutant, pin):
+    monkeypatch.setitem(O.__dict__, "_orig_attend", O.attend_dense_masked)
+    monkeypatch.setattr(O, target, mutant)
+    pins = {
+        "centroid": lambda: test_pool_centroid((31, 22, 40), (4, 8, 8), 0),
+        "ties": test_select_ties_go_to_lower_index,
+        "brute_prefix": lambda: test_brute_force_per_token(*BRUTE_CASES[3]),
+        "brute_padded": lambda: test_brute_force_per_token(*BRUTE_CASES[1]),
+        "sdpa": lambda: test_all_blocks_equals_dense_sdpa((5, 6, 7), (2, 4, 4), 0, 32),
+    }
+    with pytest.raises(AssertionError):
+        pins[pin]()
