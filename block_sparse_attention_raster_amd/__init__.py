@@ -1,0 +1,172 @@
+"""Top-k block-sparse attention over a raster-ordered (T, H, W) latent grid,
+for AMD Instinct MI355X (gfx950).
+
+Every step runs in the HIP library libvsa.so (include/vsa.h); this module
+only checks tensors and passes pointers, strides and the current stream.
+PyTorch provides device memory and streams. Importing the package does not
+load the library; the first call does, and raises if it is missing.
+
+    import block_sparse_attention_raster_amd as vsa
+    out = vsa.forward(q, k, v, latent_shape=(31, 22, 40), cube_shape=(4, 8, 8), topk=64)
+
+q, k, v: bfloat16 CUDA (HIP) tensors [B, heads, N, head_dim] with the last
+dimension contiguous and N = prefix_len + T*H*W tokens in raster order.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+from . import _lib
+from ._lib import VsaError
+
+__all__ = ["Plan", "VsaError", "plan", "plan_for", "select", "attend", "forward", "describe"]
+
+
+class Plan:
+    """A validated problem and its derived geometry (a copy of vsa_plan_t)."""
+
+    def __init__(self, raw: _lib.VsaPlan):
+        self.raw = raw
+
+    def __getattr__(self, name):
+        raw = self.__dict__["raw"]
+        if hasattr(raw, name):
+            v = getattr(raw, name)
+            return tuple(v) if name == "nblk" else v
+        if hasattr(raw.p, name):
+            v = getattr(raw.p, name)
+            return tuple(v) if name in ("latent", "cube") else v
+        raise AttributeError(name)
+
+    def valid_counts(self):
+        """Valid token count of every query block (prefix blocks, then
+        cubes), from the plan's geometry. Host-side, numpy."""
+        import numpy as np
+        T, H, W = self.latent
+        ct, ch, cw = self.cube
+        V, P = self.cube_volume, self.prefix_len
+        pre = [min(V, P - i * V) for i in range(self.num_prefix_blocks)]
+        ax = [np.minimum(c, L - np.arange(n) * c) for L, c, n in zip((T, H, W), (ct, ch, cw), self.nblk)]
+        vid = (ax[0][:, None, None] * ax[1][None, :, None] * ax[2][None, None, :]).reshape(-1)
+        return np.concatenate([np.array(pre, dtype=np.int64), vid.astype(np.int64)])
+
+    def __repr__(self):
+        return f"Plan({describe(self)})"
+
+
+def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Sequence[int], topk: int,
+         prefix_len: int = 0, strides: Optional[Sequence[int]] = None,
+         o_strides: Optional[Sequence[int]] = None) -> Plan:
+    """Validate a problem and derive its geometry (vsa_plan). ``strides``
+    are the (b, h, n) element strides shared by q, k and v; the default is
+    a contiguous [B, heads, N, head_dim] layout. ``o_strides`` default to
+    ``strides``."""
+    N = int(prefix_len) + int(latent[0]) * int(latent[1]) * int(latent[2])
+    if strides is None:
+        strides = (heads * N * head_dim, N * head_dim, head_dim)
+    if o_strides is None:
+        o_strides = strides
+    pr = _lib.VsaProblem()
+    pr.batch, pr.heads, pr.head_dim = int(batch), int(heads), int(head_dim)
+    pr.latent[:] = [int(x) for x in latent]
+    pr.cube[:] = [int(x) for x in cube]
+    pr.topk, pr.prefix_len, pr.dtype = int(topk), int(prefix_len), _lib.VSA_DTYPE_BF16
+    pr.stride_b, pr.stride_h, pr.stride_n = (int(s) for s in strides)
+    pr.o_stride_b, pr.o_stride_h, pr.o_stride_n = (int(s) for s in o_strides)
+    raw = _lib.VsaPlan()
+    _lib.check(_lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(raw)), "vsa_plan")
+    return Plan(raw)
+
+
+def _check_qkv(t, name, shape, strides):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.stride(3) != 1 or tuple(t.stride()[:3]) != tuple(strides):
+        raise ValueError(f"{name} strides {t.stride()} do not match the plan's {tuple(strides)} "
+                         "(head_dim must be contiguous)")
+
+
+def plan_for(q, latent: Sequence[int], cube: Sequence[int], topk: int, prefix_len: int = 0,
+             out=None) -> Plan:
+    """Plan from q's shape and strides (and out's strides, if given)."""
+    B, Hh, N, D = q.shape
+    o_strides = out.stride()[:3] if out is not None else q.stride()[:3]
+    return plan(B, Hh, D, latent, cube, topk, prefix_len, q.stride()[:3], o_strides)
+
+
+def _stream_ptr(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def select(pl: Plan, q, k, workspace=None, sel=None):
+    """Pool, score and select (vsa_select). Returns (sel, workspace):
+    sel int32 [B, heads, num_q_blocks, topk] ascending cube ids; workspace
+    holds float32 qbar then kbar (see include/vsa.h)."""
+    import torch
+    shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
+    strides = (pl.stride_b, pl.stride_h, pl.stride_n)
+    _check_qkv(q, "q", shape, strides)
+    _check_qkv(k, "k", shape, strides)
+    dev = q.device
+    if workspace is None:
+        workspace = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < pl.workspace_bytes or not workspace.is_contiguous():
+        raise ValueError("workspace too small or not contiguous")
+    if sel is None:
+        sel = torch.empty((pl.batch, pl.heads, pl.num_q_blocks, pl.topk), dtype=torch.int32, device=dev)
+    elif sel.dtype != torch.int32 or sel.numel() != pl.sel_elems or not sel.is_contiguous():
+        raise ValueError("sel must be a contiguous int32 tensor of plan.sel_elems elements")
+    with torch.cuda.device(dev):
+        st = _lib.lib().vsa_select(ctypes.byref(pl.raw), q.data_ptr(), k.data_ptr(), workspace.data_ptr(),
+                                   sel.data_ptr(), _stream_ptr(dev))
+    _lib.check(st, "vsa_select")
+    return sel, workspace
+
+
+def attend(pl: Plan, q, k, v, sel, out=None):
+    """Block-sparse attention over the kept blocks (vsa_attend)."""
+    import torch
+    shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
+    strides = (pl.stride_b, pl.stride_h, pl.stride_n)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_qkv(t, n, shape, strides)
+    dev = q.device
+    if out is None:
+        out = torch.empty_strided(shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n, 1),
+                                  dtype=torch.bfloat16, device=dev)
+    else:
+        _check_qkv(out, "out", shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n))
+    if sel.dtype != torch.int32 or sel.numel() != pl.sel_elems or not sel.is_contiguous():
+        raise ValueError("sel must be a contiguous int32 tensor of plan.sel_elems elements")
+    with torch.cuda.device(dev):
+        st = _lib.lib().vsa_attend(ctypes.byref(pl.raw), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   sel.data_ptr(), out.data_ptr(), _stream_ptr(dev))
+    _lib.check(st, "vsa_attend")
+    return out
+
+
+def forward(q, k, v, latent_shape: Sequence[int], cube_shape: Sequence[int], topk: int,
+            prefix_len: int = 0, out=None, return_sel: bool = False):
+    """Select then attend on the current stream. Returns out (and sel)."""
+    pl = plan_for(q, latent_shape, cube_shape, topk, prefix_len, out)
+    sel, _ = select(pl, q, k)
+    out = attend(pl, q, k, v, sel, out)
+    return (out, sel) if return_sel else out
+
+
+def describe(pl: Plan) -> str:
+    """The Wan routing-log fields for this plan (vsa_describe)."""
+    buf = ctypes.create_string_buffer(512)
+    n = _lib.lib().vsa_describe(ctypes.byref(pl.raw), buf, len(buf))
+    if n < 0:
+        raise VsaError(n, "vsa_describe")
+    return buf.value.decode()

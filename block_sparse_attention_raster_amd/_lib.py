@@ -1,0 +1,90 @@
+"""ctypes view of libvsa.so's C ABI (include/vsa.h). Marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvsa.so")
+
+VSA_OK = 0
+VSA_ERR_INVALID_ARG = -1
+VSA_ERR_TOPK = -2
+VSA_ERR_UNSUPPORTED = -3
+VSA_ERR_ALIGN = -4
+VSA_ERR_OVERFLOW = -5
+VSA_ERR_DEVICE = -6
+VSA_ERR_LAUNCH = -7
+VSA_DTYPE_BF16 = 0
+
+EXPORTED = ("vsa_plan", "vsa_select", "vsa_attend", "vsa_forward", "vsa_describe",
+            "vsa_status_str")
+
+
+class VsaProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("latent", ctypes.c_int32 * 3), ("cube", ctypes.c_int32 * 3),
+        ("topk", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+        ("o_stride_b", ctypes.c_int64), ("o_stride_h", ctypes.c_int64), ("o_stride_n", ctypes.c_int64),
+    ]
+
+
+class VsaPlan(ctypes.Structure):
+    _fields_ = [
+        ("p", VsaProblem),
+        ("nblk", ctypes.c_int32 * 3),
+        ("num_blocks", ctypes.c_int32), ("num_prefix_blocks", ctypes.c_int32),
+        ("num_q_blocks", ctypes.c_int32), ("cube_volume", ctypes.c_int32),
+        ("seq_len", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+        ("kbar_offset", ctypes.c_int64), ("sel_elems", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("select_rows", ctypes.c_int32), ("attend_variant", ctypes.c_int32),
+        ("attend_tiles", ctypes.c_int32),
+    ]
+
+
+class VsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvsa.so once. Raises if it has not been built: there is no
+    fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with "
+                "`python -m block_sparse_attention_raster_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.vsa_plan.argtypes = [ctypes.POINTER(VsaProblem), ctypes.POINTER(VsaPlan)]
+        L.vsa_plan.restype = ctypes.c_int
+        L.vsa_select.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp]
+        L.vsa_select.restype = ctypes.c_int
+        L.vsa_attend.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp, vp]
+        L.vsa_attend.restype = ctypes.c_int
+        L.vsa_forward.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp, vp, vp]
+        L.vsa_forward.restype = ctypes.c_int
+        L.vsa_describe.argtypes = [ctypes.POINTER(VsaPlan), ctypes.c_char_p, ctypes.c_size_t]
+        L.vsa_describe.restype = ctypes.c_int
+        L.vsa_status_str.argtypes = [ctypes.c_int]
+        L.vsa_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().vsa_status_str(int(status)).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != VSA_OK:
+        raise VsaError(status, where)

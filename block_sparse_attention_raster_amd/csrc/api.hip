@@ -1,0 +1,137 @@
+// extern "C" entry points of the block-sparse attention library: argument
+// checks, the gfx950 device check and kernel launches on the caller's
+// stream. No allocation, no synchronisation.
+
+#include <atomic>
+#include <cstring>
+
+#include "vsa.h"
+#include "vsa_device.h"
+#include "vsa_limits.h"
+
+hipError_t vsa_launch_pool(const VsaArgs& a, const void* q, const void* k, float* qbar, float* kbar,
+                           hipStream_t stream);
+hipError_t vsa_launch_score_topk(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel,
+                                 hipStream_t stream);
+size_t vsa_select_lds_bytes(const VsaArgs& a);
+hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
+                             const int32_t* sel, void* o, hipStream_t stream);
+hipError_t vsa_prepare_select(size_t lds_bytes);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VSA_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (known != 0) return known > 0 ? VSA_OK : VSA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VSA_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  return ok ? VSA_OK : VSA_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Re-validates a caller-held plan (it is plain data and could be edited) by
+// planning its problem again and comparing the derived fields.
+int check_plan(const vsa_plan_t* plan) {
+  if (plan == nullptr) return VSA_ERR_INVALID_ARG;
+  vsa_plan_t fresh;
+  const int st = vsa_plan(&plan->p, &fresh);
+  if (st != VSA_OK) return st;
+  const bool same =
+      fresh.nblk[0] == plan->nblk[0] && fresh.nblk[1] == plan->nblk[1] && fresh.nblk[2] == plan->nblk[2] &&
+      fresh.num_blocks == plan->num_blocks && fresh.num_prefix_blocks == plan->num_prefix_blocks &&
+      fresh.num_q_blocks == plan->num_q_blocks && fresh.cube_volume == plan->cube_volume &&
+      fresh.seq_len == plan->seq_len && fresh.workspace_bytes == plan->workspace_bytes &&
+      fresh.kbar_offset == plan->kbar_offset && fresh.sel_elems == plan->sel_elems &&
+      fresh.scale == plan->scale && fresh.select_rows == plan->select_rows &&
+      fresh.attend_variant == plan->attend_variant && fresh.attend_tiles == plan->attend_tiles;
+  return same ? VSA_OK : VSA_ERR_INVALID_ARG;
+}
+
+VsaArgs make_args(const vsa_plan_t& pl) {
+  const vsa_problem& p = pl.p;
+  VsaArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = p.batch;
+  a.Hh = p.heads;
+  a.D = p.head_dim;
+  a.T = p.latent[0];
+  a.H = p.latent[1];
+  a.W = p.latent[2];
+  a.ct = p.cube[0];
+  a.ch = p.cube[1];
+  a.cw = p.cube[2];
+  a.nT = pl.nblk[0];
+  a.nH = pl.nblk[1];
+  a.nW = pl.nblk[2];
+  a.P = p.prefix_len;
+  a.V = pl.cube_volume;
+  a.Pb = pl.num_prefix_blocks;
+  a.nb = pl.num_blocks;
+  a.nq = pl.num_q_blocks;
+  a.topk = p.topk;
+  a.sb = p.stride_b;
+  a.sh = p.stride_h;
+  a.sn = (int32_t)p.stride_n;
+  a.osb = p.o_stride_b;
+  a.osh = p.o_stride_h;
+  a.osn = (int32_t)p.o_stride_n;
+  a.scale_log2e = pl.scale * 1.4426950408889634f;
+  a.select_rows = pl.select_rows;
+  a.tiles = pl.attend_tiles;
+  return a;
+}
+
+}  // namespace
+
+extern "C" int vsa_select(const vsa_plan_t* plan, const void* q, const void* k, void* workspace,
+                          int32_t* sel, void* stream) {
+  int st = check_plan(plan);
+  if (st != VSA_OK) return st;
+  if (q == nullptr || k == nullptr || workspace == nullptr || sel == nullptr) return VSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      (reinterpret_cast<uintptr_t>(sel) & 3u) != 0)
+    return VSA_ERR_ALIGN;
+  if ((st = check_device()) != VSA_OK) return st;
+  const VsaArgs a = make_args(*plan);
+  float* qbar = static_cast<float*>(workspace);
+  float* kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->kbar_offset);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (vsa_prepare_select(vsa_select_lds_bytes(a)) != hipSuccess) return VSA_ERR_LAUNCH;
+  if (vsa_launch_pool(a, q, k, qbar, kbar, s) != hipSuccess) return VSA_ERR_LAUNCH;
+  if (vsa_launch_score_topk(a, qbar, kbar, sel, s) != hipSuccess) return VSA_ERR_LAUNCH;
+  return VSA_OK;
+}
+
+extern "C" int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+                          const int32_t* sel, void* o, void* stream) {
+  int st = check_plan(plan);
+  if (st != VSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || sel == nullptr || o == nullptr)
+    return VSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(sel) & 3u) != 0)
+    return VSA_ERR_ALIGN;
+  if ((st = check_device()) != VSA_OK) return st;
+  const VsaArgs a = make_args(*plan);
+  if (vsa_launch_attend(a, plan->attend_variant, q, k, v, sel, o, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return VSA_ERR_LAUNCH;
+  return VSA_OK;
+}
+
+extern "C" int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+                           void* workspace, int32_t* sel, void* o, void* stream) {
+  const int st = vsa_select(plan, q, k, workspace, sel, stream);
+  if (st != VSA_OK) return st;
+  return vsa_attend(plan, q, k, v, sel, o, stream);
+}

@@ -1,0 +1,89 @@
+// Device-side types and the raster <-> block index map shared by the
+// block-sparse attention kernels (gfx950, wave64).
+//
+// Index map (fastbsa package page, section "How it works": the raster to
+// block-contiguous map is evaluated inside the kernels, so q, k and v are
+// never permuted through HBM). A block's tokens are addressed by a compact
+// slot r in 0..n-1, where n is the number of valid tokens: for a video cube
+// with valid extents (et, eh, ew) slot r is (tt, hh, ww) in raster order
+// inside the cube, token row P + ((t0+tt)*H + h0+hh)*W + w0+ww; for prefix
+// block p slot r is token row p*V + r. Partial edge cubes therefore have no
+// holes: only the last 64-token tile of a block can be short.
+#ifndef VSA_DEVICE_H
+#define VSA_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Everything the kernels need, passed by value.
+struct VsaArgs {
+  int32_t B, Hh, D;
+  int32_t T, H, W;
+  int32_t ct, ch, cw;
+  int32_t nT, nH, nW;
+  int32_t P, V, Pb, nb, nq;
+  int32_t topk;
+  int64_t sb, sh;  // q/k/v batch and head strides (elements)
+  int32_t sn;      // q/k/v token stride (elements)
+  int64_t osb, osh;
+  int32_t osn;
+  float scale_log2e;     // head_dim^-1/2 * log2(e)
+  int32_t select_rows;   // query blocks per score/top-k workgroup
+  int32_t tiles;         // query row tiles per query block
+};
+
+// Valid region of one block: first token row, extents of the (tt, hh, ww)
+// box (prefix blocks use (1, 1, n)) and valid token count.
+struct BlockExt {
+  int32_t base;
+  int32_t eh, ew;
+  int32_t n;
+};
+
+__device__ __forceinline__ BlockExt block_ext(const VsaArgs& a, int32_t blk) {
+  BlockExt e;
+  if (blk < a.Pb) {
+    const int32_t s = blk * a.V;
+    const int32_t n = min(a.V, a.P - s);
+    e.base = s;
+    e.eh = 1;
+    e.ew = n;
+    e.n = n;
+    return e;
+  }
+  const int32_t c = blk - a.Pb;
+  const int32_t bw = c % a.nW;
+  const int32_t rest = c / a.nW;
+  const int32_t bh = rest % a.nH;
+  const int32_t bt = rest / a.nH;
+  const int32_t t0 = bt * a.ct, h0 = bh * a.ch, w0 = bw * a.cw;
+  const int32_t et = min(a.ct, a.T - t0);
+  e.eh = min(a.ch, a.H - h0);
+  e.ew = min(a.cw, a.W - w0);
+  e.base = a.P + (t0 * a.H + h0) * a.W + w0;
+  e.n = et * e.eh * e.ew;
+  return e;
+}
+
+// Token row of compact slot r (0 <= r < e.n) of a block.
+__device__ __forceinline__ int32_t slot_row(const VsaArgs& a, const BlockExt& e, int32_t r) {
+  const uint32_t ehw = (uint32_t)(e.eh * e.ew);
+  const uint32_t tt = (uint32_t)r / ehw;
+  const uint32_t rem = (uint32_t)r - tt * ehw;
+  const uint32_t hh = rem / (uint32_t)e.ew;
+  const uint32_t ww = rem - hh * (uint32_t)e.ew;
+  return e.base + ((int32_t)tt * a.H + (int32_t)hh) * a.W + (int32_t)ww;
+}
+
+__device__ __forceinline__ uint32_t orderable_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+#endif

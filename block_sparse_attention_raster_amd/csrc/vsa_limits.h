@@ -1,0 +1,15 @@
+// Internal limits and tiling codes shared by the host plan and the launchers.
+#ifndef VSA_LIMITS_H
+#define VSA_LIMITS_H
+
+#define VSA_MAX_CUBE_VOLUME 1024      /* tokens per block                      */
+#define VSA_MAX_BLOCKS 16384          /* video cubes per (batch, head)         */
+#define VSA_SELECT_MAX_ROWS 16        /* query blocks per score/top-k group    */
+#define VSA_SELECT_SCORE_LDS 65536    /* bytes of LDS for one group's scores   */
+
+enum {
+  VSA_ATTEND_ROWS64 = 1,   /* 64 query rows per workgroup (cubes <= 64 tokens) */
+  VSA_ATTEND_ROWS128 = 2   /* 128 query rows per workgroup                     */
+};
+
+#endif

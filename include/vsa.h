@@ -1,0 +1,156 @@
+/*
+ * vsa.h - C ABI of a top-k block-sparse attention library for AMD Instinct
+ * MI355X (gfx950) over a raster-ordered (T, H, W) video latent grid.
+ *
+ * The operation (pages: "FastVideo VSA" user guide of vllm-omni, opening
+ * definition and section "Wan top-k behavior"; "fastbsa" package page,
+ * sections "Use" and "How it works"):
+ *
+ *   The N = P + T*H*W tokens of each (batch, head) are q, k, v rows in
+ *   raster order: P optional prefix tokens first, then grid point (t, h, w)
+ *   at row P + (t*H + h)*W + w. The grid is cut into cubes of ct x ch x cw
+ *   tokens (cubes at the far edge of an axis hold fewer), numbered in raster
+ *   order of the cube grid; the prefix forms ceil(P / V) blocks of
+ *   V = ct*ch*cw tokens, always kept. Every query block (prefix blocks first,
+ *   then cubes) is scored against every cube by
+ *       s[i][j] = mean_q(i) . mean_k(j) * head_dim^-1/2
+ *   (means over the block's valid tokens), keeps its topk highest-scoring
+ *   cubes (equal scores: lower cube id first), and each of its query tokens
+ *   runs exact softmax attention, scale head_dim^-1/2, over the tokens of
+ *   the kept cubes and of all prefix blocks.
+ *
+ * Data types and layouts
+ *   q, k, v, o   bfloat16, element (b, h, n, d) at
+ *                b*stride_b + h*stride_h + n*stride_n + d   (elements);
+ *                d is contiguous. q, k and v share one set of strides; o has
+ *                its own. Base pointers and strides*2 must be multiples of
+ *                16 bytes.
+ *   workspace    float32 pooled means, written by vsa_select:
+ *                  qbar [B][Hh][num_q_blocks][head_dim], then
+ *                  kbar [B][Hh][num_blocks][head_dim] at byte offset
+ *                  plan.kbar_offset. Size plan.workspace_bytes.
+ *   sel          int32 [B][Hh][num_q_blocks][topk], ascending cube ids in
+ *                0 .. num_blocks-1. Prefix blocks are kept implicitly and
+ *                never appear in sel.
+ *
+ * Ownership and execution
+ *   The caller allocates and owns every buffer (device memory for q, k, v,
+ *   o, sel and workspace; host memory for the problem and plan structs).
+ *   The library allocates nothing and keeps no per-call state, so calls on
+ *   different streams may run concurrently on different buffers. Device
+ *   work is enqueued on the given HIP stream (NULL = the null stream) and
+ *   is asynchronous: no call synchronises, and a device fault surfaces at
+ *   the caller's next synchronisation. Errors found on the host are
+ *   returned before anything is enqueued. No entry point throws.
+ *
+ * There is no dense fallback: inputs the kernels cannot take return an
+ * error code and the caller decides what to do.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. 0 is success; errors are negative. */
+enum {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARG = -1,  /* null pointer, a size <= 0, prefix_len < 0   */
+  VSA_ERR_TOPK = -2,         /* topk < 1 or topk > num_blocks (the user
+                                guide: top-k must be positive and may not
+                                exceed the block count)                     */
+  VSA_ERR_UNSUPPORTED = -3,  /* head_dim not 64 or 128, dtype not bf16,
+                                cube volume > 1024, num_blocks > 16384      */
+  VSA_ERR_ALIGN = -4,        /* pointer or stride not 16-byte aligned       */
+  VSA_ERR_OVERFLOW = -5,     /* an element offset or a count would overflow
+                                the kernels' index types                    */
+  VSA_ERR_DEVICE = -6,       /* current device is not gfx950, or a HIP
+                                query failed                                */
+  VSA_ERR_LAUNCH = -7        /* a kernel launch reported an error           */
+};
+
+enum { VSA_DTYPE_BF16 = 0 };
+
+/* What the caller asks for. All sizes in elements or tokens. */
+typedef struct vsa_problem {
+  int32_t batch;          /* B  >= 1                                         */
+  int32_t heads;          /* Hh >= 1 (q, k and v have equal head counts)     */
+  int32_t head_dim;       /* D: 64 or 128                                    */
+  int32_t latent[3];      /* (T, H, W) grid, each >= 1                       */
+  int32_t cube[3];        /* (ct, ch, cw) block shape, each >= 1            */
+  int32_t topk;           /* cubes kept per query block, 1..num_blocks       */
+  int32_t prefix_len;     /* P >= 0 tokens before the grid, always kept      */
+  int32_t dtype;          /* VSA_DTYPE_BF16                                  */
+  int64_t stride_b, stride_h, stride_n;        /* q, k, v strides (elements) */
+  int64_t o_stride_b, o_stride_h, o_stride_n;  /* o strides (elements)       */
+} vsa_problem;
+
+/* Derived geometry; filled by vsa_plan, plain data, owned by the caller. */
+typedef struct vsa_plan_t {
+  vsa_problem p;
+  int32_t nblk[3];            /* cubes per axis: ceil(T/ct), ceil(H/ch), ceil(W/cw) */
+  int32_t num_blocks;         /* video cubes nT*nH*nW                        */
+  int32_t num_prefix_blocks;  /* ceil(P / V)                                 */
+  int32_t num_q_blocks;       /* num_prefix_blocks + num_blocks              */
+  int32_t cube_volume;        /* V = ct*ch*cw                                */
+  int64_t seq_len;            /* N = P + T*H*W                               */
+  int64_t workspace_bytes;    /* bytes of float32 workspace vsa_select needs */
+  int64_t kbar_offset;        /* byte offset of kbar inside the workspace    */
+  int64_t sel_elems;          /* B*Hh*num_q_blocks*topk                      */
+  float scale;                /* head_dim^-1/2                               */
+  int32_t select_rows;        /* query blocks per score/top-k workgroup      */
+  int32_t attend_variant;     /* attention kernel tiling chosen by the plan  */
+  int32_t attend_tiles;       /* query row tiles per query block             */
+} vsa_plan_t;
+
+/* Validate a problem and derive its geometry. Host only: no device work,
+ * no allocation. Returns VSA_OK and fills *out, or an error code and leaves
+ * *out unspecified. The Wan routing-log shape (31, 22, 40) with (4, 8, 8)
+ * cubes gives num_blocks = 120 (user guide, "Wan top-k behavior"). */
+int vsa_plan(const vsa_problem* problem, vsa_plan_t* out);
+
+/* Block selection (pages: user guide opening definition; fastbsa "How it
+ * works": the score matrix never leaves on-chip memory). Pools q over every
+ * query block and k over every cube into the workspace, then scores every
+ * query block against every cube and writes its topk cube ids, ascending,
+ * to sel. q, k: device bf16 per the plan's strides. workspace: device,
+ * >= plan->workspace_bytes, 256-byte aligned. sel: device int32,
+ * plan->sel_elems. stream: hipStream_t or NULL. Asynchronous. */
+int vsa_select(const vsa_plan_t* plan, const void* q, const void* k,
+               void* workspace, int32_t* sel, void* stream);
+
+/* Block-sparse attention (pages: user guide opening definition; fastbsa
+ * "How it works": raster-to-block index map evaluated inside the kernel).
+ * For every query token, exact softmax attention over the tokens of all
+ * prefix blocks and of the cubes listed in sel for its query block; o is
+ * written in the same raster layout as q (o_stride_*). sel must hold valid
+ * ascending ids as vsa_select writes them (other contents give undefined
+ * output but stay in bounds: ids are clamped to 0..num_blocks-1). o must
+ * not alias q, k or v. Asynchronous. */
+int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k,
+               const void* v, const int32_t* sel, void* o, void* stream);
+
+/* vsa_select followed by vsa_attend on the same stream. */
+int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k,
+                const void* v, void* workspace, int32_t* sel, void* o,
+                void* stream);
+
+/* Formats the routing fields of the user guide's Wan log line
+ * ("seq_len=..., dit_seq_shape=(T, H, W), block_size=(ct, ch, cw),
+ * num_blocks=..., topk=..., keep_ratio=..%") into buf (always
+ * NUL-terminated when len > 0). Returns the length the full string needs,
+ * excluding the NUL, or a negative error code. */
+int vsa_describe(const vsa_plan_t* plan, char* buf, size_t len);
+
+/* Static description of a status code; never NULL. */
+const char* vsa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

@@ -1,0 +1,189 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Selection is compared with the oracle's float64 scores, bit-exact except
+for ids whose scores lie within 1e-6 of the row's k-th score. Outputs are
+compared with the oracle's dense-masked attention recomputed under the
+GPU's own selection: max-abs <= 2e-2 and relative L2 <= 1e-2.
+
+Small cases run the whole oracle; the full-size workloads check every
+selection row and the outputs of sampled query blocks (always including the
+first, the last and partial-edge blocks).
+"""
+import functools
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_raster_amd import synthetic
+from oracle import vsa_oracle as O
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _full_check(w, topk, heads=None, blocks_per_head=None):
+    _announce(f"{w.name}: B={w.batch} Hh={w.heads} D={w.head_dim} grid={w.latent} cube={w.cube} "
+              f"P={w.prefix_len} topk={topk}")
+    res = G.run_gpu(w, topk, _inputs(w))
+    g, qbar, kbar, scores = G.oracle_scores(w, res["bits"][0], res["bits"][1])
+    # pooled means: float32 GPU vs float64 oracle
+    np.testing.assert_allclose(res["qbar"], qbar, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(res["kbar"], kbar, rtol=1e-5, atol=1e-5)
+    chk = O.check_selection(res["sel"], scores, topk, band=G.TIE_BAND)
+    assert chk["mismatch_rows"] == [], f"selection mismatches in rows {chk['mismatch_rows'][:10]}"
+    if heads is None:
+        heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    worst = G.check_outputs(w, g, res, heads, blocks_per_head)
+    _announce(f"{w.name}/topk{topk}: band rows {chk['band_rows']} of {chk['rows']}, "
+              f"max_abs {worst['max_abs']:.3e} rel_l2 {worst['rel_l2']:.3e}")
+    assert worst["max_abs"] <= G.MAX_ABS
+    assert worst["rel_l2"] <= G.REL_L2
+    return res, g
+
+
+@functools.lru_cache(maxsize=2)
+def _inputs(w):
+    return synthetic.make_inputs(w)
+
+
+SMALL = [
+    # name, B, Hh, D, latent, cube, topk, prefix
+    ("tiny_grid_d64", 1, 2, 64, (8, 8, 8), (4, 4, 4), 4, 0),
+    ("ragged_axes_v32", 2, 2, 128, (5, 6, 7), (2, 4, 4), 5, 0),
+    ("wan_cube_ragged", 1, 2, 128, (9, 10, 11), (4, 8, 8), 3, 0),
+    ("wan_cube_ragged_d64", 1, 3, 64, (9, 10, 11), (4, 8, 8), 5, 0),
+    ("prefix_partial_block", 2, 2, 128, (6, 7, 9), (4, 4, 4), 5, 100),
+    ("prefix_v256", 1, 2, 128, (5, 9, 17), (4, 8, 8), 2, 300),
+    ("cube_bigger_than_grid", 1, 2, 128, (3, 5, 7), (4, 8, 8), 1, 0),
+    ("all_blocks_dense", 1, 2, 128, (9, 10, 11), (4, 8, 8), 12, 0),
+    ("topk_one", 1, 2, 128, (8, 12, 16), (4, 4, 4), 1, 0),
+    ("tiny_cubes", 1, 2, 128, (3, 4, 5), (1, 2, 2), 7, 3),
+    ("odd_cube_v60", 1, 2, 64, (7, 9, 10), (3, 4, 5), 4, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_case_full_oracle(case):
+    name, B, Hh, D, latent, cube, topk, P = case
+    w = synthetic.custom_workload(name, seed=zlib.crc32(name.encode()) & 0xFFFF, batch=B, heads=Hh, head_dim=D,
+                                  latent=latent, cube=cube, topk=topk, prefix_len=P)
+    _full_check(w, topk)
+
+
+def test_all_blocks_equals_dense_attention():
+    """topk == num_blocks: the sparse path must give dense attention."""
+    import torch
+    w = synthetic.custom_workload("dense", seed=7, batch=1, heads=2, head_dim=128,
+                                  latent=(9, 10, 11), cube=(4, 8, 8), topk=12)
+    _announce("all-blocks vs dense softmax attention")
+    res = G.run_gpu(w, 12)
+    for h in range(2):
+        q, k, v = (torch.from_numpy(O.decode_bf16(x[0, h]))[None, None] for x in res["bits"])
+        dense = torch.nn.functional.scaled_dot_product_attention(q, k, v)[0, 0].numpy()
+        e = O.error_norms(res["out"][0, h], dense)
+        assert e["max_abs"] <= G.MAX_ABS and e["rel_l2"] <= G.REL_L2, e
+
+
+def test_constant_values_give_constant_output():
+    """V == 1 everywhere: each softmax row sums to one, so O == 1 exactly in
+    bf16 up to the rounding of the normaliser."""
+    w = synthetic.custom_workload("ones", seed=8, batch=1, heads=2, head_dim=128,
+                                  latent=(9, 10, 11), cube=(4, 8, 8), topk=5, prefix_len=40)
+    q_b, k_b, v_b = synthetic.make_inputs(w)
+    v_b = np.full_like(v_b, 0x3F80)
+    _announce("constant V")
+    res = G.run_gpu(w, 5, (q_b, k_b, v_b))
+    assert np.max(np.abs(res["out"] - 1.0)) <= 2 ** -7
+
+
+def test_pool_centroid_through_workspace():
+    """q, k hold each token's (t, h, w) coordinates: the pooled means in the
+    workspace are the centroids of the valid parts of the blocks."""
+    w = synthetic.custom_workload("centroid", seed=9, batch=1, heads=1, head_dim=64,
+                                  latent=(31, 22, 40), cube=(4, 8, 8), topk=3, prefix_len=0)
+    T, H, W = w.latent
+    x = np.zeros((1, 1, T * H * W, 64), dtype=np.float32)
+    t, hh, ww = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    x[0, 0, :, 0], x[0, 0, :, 1], x[0, 0, :, 2] = t.ravel(), hh.ravel(), ww.ravel()
+    bits = synthetic.f32_to_bf16_bits(x)
+    _announce("pool centroid")
+    res = G.run_gpu(w, 3, (bits, bits, bits))
+    g = O.geometry(w.latent, w.cube)
+    nT, nH, nW = g.nblk
+    for bt in range(nT):
+        for bh in range(nH):
+            for bw in range(nW):
+                c = (bt * nH + bh) * nW + bw
+                for a, blk in enumerate((bt, bh, bw)):
+                    lo = blk * w.cube[a]
+                    hi = min(w.latent[a], lo + w.cube[a]) - 1
+                    assert res["qbar"][0, 0, c, a] == (lo + hi) / 2
+                    assert res["kbar"][0, 0, c, a] == (lo + hi) / 2
+    assert tuple(res["qbar"][0, 0, -1, :3]) == (29.0, 18.5, 35.5)
+
+
+def test_strided_layouts_and_repeatability():
+    """q, k, v as views of one fused [B, N, 3, Hh, D] tensor and o in
+    [B, N, Hh, D]: same result as the contiguous layout, bit for bit, and
+    two runs agree bit for bit."""
+    import torch
+    import block_sparse_attention_raster_amd as vsa
+    w = synthetic.custom_workload("strided", seed=10, batch=2, heads=3, head_dim=128,
+                                  latent=(5, 9, 17), cube=(4, 8, 8), topk=3, prefix_len=20)
+    q_b, k_b, v_b = synthetic.make_inputs(w)
+    _announce("strided layouts")
+    q, k, v = (G.to_device(x) for x in (q_b, k_b, v_b))
+    ref, sel_ref = vsa.forward(q, k, v, w.latent, w.cube, 3, w.prefix_len, return_sel=True)
+    again, sel_again = vsa.forward(q, k, v, w.latent, w.cube, 3, w.prefix_len, return_sel=True)
+    fused = torch.stack([q, k, v], dim=0).permute(1, 3, 0, 2, 4).contiguous()   # [B, N, 3, Hh, D]
+    qs, ks, vs = (fused[:, :, i].permute(0, 2, 1, 3) for i in range(3))           # [B, Hh, N, D] views
+    out = torch.empty((w.batch, w.seq_len, w.heads, w.head_dim), dtype=torch.bfloat16,
+                      device="cuda").permute(0, 2, 1, 3)
+    got, sel_got = vsa.forward(qs, ks, vs, w.latent, w.cube, 3, w.prefix_len, out=out, return_sel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_ref, sel_again) and torch.equal(ref, again)
+    assert torch.equal(sel_ref, sel_got)
+    assert torch.equal(ref, got)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: every selection row, sampled output blocks
+# ---------------------------------------------------------------------------
+
+def test_workload_tiny_full():
+    _full_check(synthetic.WORKLOADS["tiny"], 4)
+
+
+def test_workload_wan():
+    w = synthetic.WORKLOADS["wan"]
+    _full_check(w, 64, heads=[(0, 0), (0, 11), (0, 23)], blocks_per_head=6)
+
+
+@pytest.mark.parametrize("topk", [16, 32, 120])
+def test_workload_wan_sweep(topk):
+    w = synthetic.WORKLOADS["wan_sweep"]
+    _full_check(w, topk, heads=[(0, 0), (0, 17)], blocks_per_head=5)
+
+
+def test_workload_long720p():
+    w = synthetic.WORKLOADS["long720p"]
+    _full_check(w, 60, heads=[(0, 0), (0, 31)], blocks_per_head=12)
+
+
+def test_workload_prefix():
+    w = synthetic.WORKLOADS["prefix"]
+    _full_check(w, 96, heads=[(0, 0), (1, 23)], blocks_per_head=12)
