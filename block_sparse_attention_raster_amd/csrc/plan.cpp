@@ -55,6 +55,7 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   if (V > VSA_MAX_CUBE_VOLUME) return VSA_ERR_UNSUPPORTED;
   const int64_t nb = nT * nH * nW;
   if (nb > VSA_MAX_BLOCKS) return VSA_ERR_UNSUPPORTED;
+  if (ct > 1023 || ch > 1023 || cw > 1023) return VSA_ERR_UNSUPPORTED;
   const int64_t P = p.prefix_len;
   const int64_t Pb = ceil_div(P, V);
   const int64_t nq = Pb + nb;
@@ -111,8 +112,8 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
     r.attend_variant = VSA_ATTEND_ROWS64;
     r.attend_tiles = 1;
   } else {
-    r.attend_variant = VSA_ATTEND_ROWS128;
-    r.attend_tiles = (int32_t)ceil_div(V, 128);
+    r.attend_variant = VSA_ATTEND_ROWS256;
+    r.attend_tiles = (int32_t)ceil_div(V, 256);
   }
   const int64_t grid = BH * nq * r.attend_tiles;
   if (grid > (int64_t)INT32_MAX) return VSA_ERR_OVERFLOW;
