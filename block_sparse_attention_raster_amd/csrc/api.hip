@@ -13,10 +13,8 @@ hipError_t vsa_launch_pool(const VsaArgs& a, const void* q, const void* k, float
                            hipStream_t stream);
 hipError_t vsa_launch_score_topk(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel,
                                  hipStream_t stream);
-size_t vsa_select_lds_bytes(const VsaArgs& a);
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                              const int32_t* sel, void* o, hipStream_t stream);
-hipError_t vsa_prepare_select(size_t lds_bytes);
 
 namespace {
 
@@ -88,6 +86,8 @@ VsaArgs make_args(const vsa_plan_t& pl) {
   a.scale_log2e = pl.scale * 1.4426950408889634f;
   a.select_rows = pl.select_rows;
   a.tiles = pl.attend_tiles;
+  a.magic_nW = ((1ull << 32) + (uint64_t)a.nW - 1) / (uint64_t)a.nW;
+  a.magic_nH = ((1ull << 32) + (uint64_t)a.nH - 1) / (uint64_t)a.nH;
   return a;
 }
 
@@ -106,7 +106,6 @@ extern "C" int vsa_select(const vsa_plan_t* plan, const void* q, const void* k, 
   float* qbar = static_cast<float*>(workspace);
   float* kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->kbar_offset);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (vsa_prepare_select(vsa_select_lds_bytes(a)) != hipSuccess) return VSA_ERR_LAUNCH;
   if (vsa_launch_pool(a, q, k, qbar, kbar, s) != hipSuccess) return VSA_ERR_LAUNCH;
   if (vsa_launch_score_topk(a, qbar, kbar, sel, s) != hipSuccess) return VSA_ERR_LAUNCH;
   return VSA_OK;

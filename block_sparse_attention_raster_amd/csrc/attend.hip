@@ -13,16 +13,20 @@
 // numbered s = (tt*ch + hh)*cw + ww. At start-up the workgroup tabulates,
 // for every slot, its row offset (tt*H + hh)*W + ww from the cube's first
 // token and its packed (tt, hh, ww); afterwards a slot's token row is one LDS
-// read plus an add, with no division. A slot is valid when (tt, hh, ww) lies
-// inside the block's valid extents (partial cubes at the far edge of an axis);
-// prefix block slots are the rows p*V + s, valid below the prefix length.
-// Invalid key slots load as zero and are masked to -inf, so only tiles of
-// partial blocks pay for masking; a block's tiles stop at its last valid slot.
+// read plus an add. A slot is valid when (tt, hh, ww) lies inside the
+// block's valid extents (partial cubes at the far edge of an axis); prefix
+// block slots are rows p*V + s, valid below the prefix length. Invalid key
+// slots load the block's first row (finite data) and are masked to -inf, so
+// only tiles of partial blocks pay for masking; a block's tiles stop at its
+// last valid slot.
 //
-// Pipeline. K and V^T tiles are double-buffered in LDS. While tile i is
-// computed from one buffer, tile i+1's global loads are in flight into
-// registers; they are written to the other buffer after the math, followed by
-// the tile's only barrier.
+// Data movement. K and V tiles go from HBM straight into LDS with 16-byte
+// global_load_lds (no registers), NSTAGE tiles deep; each wave issues its
+// share, waits for its own loads of the tile about to be used, and one
+// barrier per tile publishes it and frees the stage the next issue reuses.
+// Both tiles keep the natural [key][head_dim] order with the 16-byte chunks
+// of each key row XOR-swizzled (applied on the global side, since the LDS
+// position of each lane's 16 bytes is fixed by its lane id).
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, lanes l = 0..63, g = l / 32):
 //   S^T = K Q^T : A = K rows (lane: key l%32, 8 head-dim values at 16c+8g),
@@ -33,13 +37,14 @@
 //                 straight from the S^T accumulators (lane: query l%32),
 //                 C: lane holds query l%32, register r holds head-dim
 //                 8*(r/4) + 4*g + r%4.
-// The 8 keys a lane feeds to one P.V step are {4g..4g+3, 8+4g..8+4g+3} of a
-// 16-key group, so V^T is stored with each 16-key group permuted as
-// (0-3, 8-11, 4-7, 12-15); one 16-byte LDS read then yields the matching V
-// operand. Every lane owns one query row: the row max and sum need one
-// exchange between the two lane halves and rescaling O is a per-lane scalar.
-// Softmax runs in base 2 on unscaled scores: p = 2^(s*c - m*c) with
-// c = head_dim^-1/2 * log2(e), the same softmax.
+// A lane feeds keys {4g..4g+3, 8+4g..8+4g+3} of a 16-key group to one P.V
+// step; the matching V^T operand comes from two ds_read_b64_tr_b16 reads of
+// the [key][head_dim] tile: in each 16-lane group, lane i addresses row
+// key0 + i/4 at head-dim column base + 4*(i%4) and lane j receives the four
+// keys key0..key0+3 of column base + j. Every lane owns one query row: row max
+// and sum need one exchange between the lane halves and rescaling O is a
+// per-lane scalar. Softmax runs in base 2 on unscaled scores:
+// p = 2^(s*c - m*c) with c = head_dim^-1/2 * log2(e), the same softmax.
 
 #include "vsa_device.h"
 #include "vsa_limits.h"
@@ -48,9 +53,18 @@ namespace {
 
 constexpr int KT = 64;  // key slots per tile
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   const __bf16 a = (__bf16)x, b = (__bf16)y;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// floor(x / d) for x, d < 2^16 with m = ceil(2^32 / d) (m = 2^32 for d = 1).
+__device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
+  return (int32_t)(((uint64_t)(uint32_t)x * m) >> 32);
 }
 
 // Packed slot coordinates: tt | hh << 10 | ww << 20 (each < 1024).
@@ -61,7 +75,7 @@ __device__ __forceinline__ bool slot_valid(uint32_t crd, uint32_t ext) {
 
 // Valid region of a kept or query block in slot space.
 struct Blk {
-  int32_t base;     // first token row
+  int32_t base;     // first token row (the row of slot 0, always valid)
   uint32_t ext;     // packed valid extents (et, eh, ew); prefix blocks (1, 1, n)
   int32_t ntiles;   // 64-slot tiles up to the last valid slot
   bool prefix;
@@ -81,10 +95,10 @@ __device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk) {
     return d;
   }
   const int32_t c = blk - a.Pb;
-  const int32_t bw = c % a.nW;
-  const int32_t rest = c / a.nW;
-  const int32_t bh = rest % a.nH;
-  const int32_t bt = rest / a.nH;
+  const int32_t rest = fast_div(c, a.magic_nW);
+  const int32_t bw = c - rest * a.nW;
+  const int32_t bt = fast_div(rest, a.magic_nH);
+  const int32_t bh = rest - bt * a.nH;
   const int32_t t0 = bt * a.ct, h0 = bh * a.ch, w0 = bw * a.cw;
   const int32_t et = min(a.ct, a.T - t0), eh = min(a.ch, a.H - h0), ew = min(a.cw, a.W - w0);
   d.base = a.P + (t0 * a.H + h0) * a.W + w0;
@@ -96,27 +110,43 @@ __device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk) {
   return d;
 }
 
-template <int D, int NW, int QB, int VCAP>
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D, int NW, int QB, int NSTAGE>
 __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
                                                              const __bf16* __restrict__ k,
                                                              const __bf16* __restrict__ v,
                                                              const int32_t* __restrict__ sel,
                                                              __bf16* __restrict__ o) {
-  constexpr int NT = NW * 64;
-  constexpr int CPR = D / 8;               // 16-byte chunks per key row
-  constexpr int RW = NW * 32 * QB;         // query slots per workgroup
-  constexpr int KCH = KT * CPR / NT;       // K chunks per thread per tile
-  constexpr int VTASKS = (KT / 2) * CPR;   // (key pair, 8 head-dim) tasks
-  constexpr int VPT = (VTASKS + NT - 1) / NT;  // V tasks per thread per tile
-  constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;  // K chunk swizzle mask
-  static_assert(KT * CPR % NT == 0, "K tile must split evenly");
+  constexpr int CPR = D / 8;             // 16-byte chunks per key row
+  constexpr int RW = NW * 32 * QB;       // query slots per workgroup
+  constexpr int UNITS = KT * CPR;        // 16-byte units per K (or V) tile
+  constexpr int SLABS = UNITS / 64;      // wave-wide loads per tensor per tile
+  constexpr int SPW = SLABS / NW;        // of which each wave issues
+  constexpr int TILE_BYTES = UNITS * 16;
+  constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;
+  static_assert(SLABS % NW == 0 && SPW >= 1, "tile loads must split evenly over the waves");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
+  constexpr int VM_PER_TILE = 2 * SPW;   // vector-memory instructions per wave per tile
 
-  __shared__ __align__(16) __bf16 Ks[2][KT * D];
-  __shared__ __align__(16) __bf16 Vt[2][D * KT];
-  __shared__ int32_t srel[VCAP];
-  __shared__ uint32_t scrd[VCAP];
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* kst = smem;                              // [NSTAGE][TILE_BYTES]
+  unsigned char* vst = smem + NSTAGE * TILE_BYTES;        // [NSTAGE][TILE_BYTES]
+  int32_t* srel = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);  // [V]
+  uint32_t* scrd = reinterpret_cast<uint32_t*>(srel + a.V);                   // [V]
 
-  int bid = blockIdx.x;
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
+  // id is remapped to give each XCD a contiguous range of (head, block) work.
+  const int nwg = a.B * a.Hh * a.nq * a.tiles;
+  const int per_xcd = (nwg + 7) / 8;
+  const int lid = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (lid >= nwg) return;
+  int bid = lid;
   const int tile = bid % a.tiles;
   bid /= a.tiles;
   const int qblk = bid % a.nq;
@@ -127,14 +157,16 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
   if (slot0 >= qd.ntiles * KT) return;
 
   const int tid = threadIdx.x;
-  for (int s = tid; s < a.V; s += NT) {
+  {
     const int chw = a.ch * a.cw;
-    const int tt = s / chw;
-    const int rem = s - tt * chw;
-    const int hh = rem / a.cw;
-    const int ww = rem - hh * a.cw;
-    srel[s] = (tt * a.H + hh) * a.W + ww;
-    scrd[s] = (uint32_t)tt | ((uint32_t)hh << 10) | ((uint32_t)ww << 20);
+    for (int s = tid; s < a.V; s += NW * 64) {
+      const int tt = s / chw;
+      const int rem = s - tt * chw;
+      const int hh = rem / a.cw;
+      const int ww = rem - hh * a.cw;
+      srel[s] = (tt * a.H + hh) * a.W + ww;
+      scrd[s] = (uint32_t)tt | ((uint32_t)hh << 10) | ((uint32_t)ww << 20);
+    }
   }
   __syncthreads();
 
@@ -186,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  // ---- kept-block walk
+  // ---- kept-block walk (issue side)
   const int nkept = a.Pb + a.topk;
   auto kept_block = [&](int i) -> int {
     if (i < a.Pb) return i;
@@ -194,104 +226,103 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
     c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
     return a.Pb + c;
   };
+  int ibi = 0, ikt = 0;
+  Blk kd = describe_block(a, kept_block(0));
 
-  u32x4 kbuf[KCH];
-  u32x4 vbuf[VPT][2];
-
-  auto load_tile = [&](const Blk& d, int t) {
+  // Issues the loads of the walker's current tile into `stage` and returns
+  // its validity mask (bit i: slot i of the tile is valid); then advances.
+  auto issue = [&](int stage) -> uint64_t {
+    const int t = ikt;
+    unsigned char* kdst = kst + stage * TILE_BYTES;
+    unsigned char* vdst = vst + stage * TILE_BYTES;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = tid + i * NT;
-      const int key = idx / CPR, c = idx % CPR;
-      const int row = slot_row(d, t * KT + key);
-      kbuf[i] = row >= 0 ? *reinterpret_cast<const u32x4*>(kh + (int64_t)row * a.sn + c * 8) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < SPW; ++j) {
+      const int s = wave * SPW + j;
+      const int p = s * 64 + lane;
+      const int key = p / CPR, cp = p % CPR;
+      int row = slot_row(kd, t * KT + key);
+      row = row < 0 ? kd.base : row;
+      const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+      const __bf16* ksrc = kh + (int64_t)row * a.sn + ((cp ^ (key & KSWZ)) * 8);
+      const __bf16* vsrc = vh + (int64_t)row * a.sn + ((cp ^ fv) * 8);
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + s * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + s * 1024), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int task = tid + i * NT;
-      const int kp = task % (KT / 2), e8 = task / (KT / 2);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = task < VTASKS ? slot_row(d, t * KT + 2 * kp + j) : -1;
-        vbuf[i][j] = row >= 0 ? *reinterpret_cast<const u32x4*>(vh + (int64_t)row * a.sn + e8 * 8)
-                              : u32x4{0, 0, 0, 0};
-      }
+    uint64_t m = ~0ull;
+    if (!(kd.full && (t + 1) * KT <= a.V)) m = __ballot(slot_row(kd, t * KT + lane) >= 0);
+    ++ikt;
+    if (ikt >= kd.ntiles) {
+      ikt = 0;
+      ++ibi;
+      if (ibi < nkept) kd = describe_block(a, kept_block(ibi));
     }
+    return m;
   };
 
-  auto store_tile = [&](int buf) {
-    __bf16* ks = Ks[buf];
-    __bf16* vt = Vt[buf];
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = tid + i * NT;
-      const int key = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<u32x4*>(ks + key * D + ((c ^ (key & KSWZ)) * 8)) = kbuf[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int task = tid + i * NT;
-      if (task >= VTASKS) break;
-      const int kp = task % (KT / 2), e8 = task / (KT / 2);
-      // keys 2kp, 2kp+1 -> positions inside the permuted 16-key group
-      const int key = 2 * kp;
-      const int p = (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
-      const int pc = p >> 3, off = p & 7;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int d = 8 * e8 + ii;
-        const uint32_t s = (ii & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w = __builtin_amdgcn_perm(vbuf[i][1][ii >> 1], vbuf[i][0][ii >> 1], s);
-        const int swz = (d ^ (d >> 3)) & 7;
-        *reinterpret_cast<uint32_t*>(vt + d * KT + ((pc ^ swz) * 8) + off) = w;
-      }
-    }
-  };
-
-  // tile validity bits (bit i: slot t*64 + i is valid), uniform
-  auto tile_mask = [&](const Blk& d, int t) -> uint64_t {
-    if (d.full && (t + 1) * KT <= a.V) return ~0ull;
-    return __ballot(slot_row(d, t * KT + lane) >= 0);
-  };
+  // per-lane LDS offsets of the MFMA operands
+  const int kswz = lane & KSWZ;                         // (32kb + l32) & KSWZ
+  const int i16 = lane & 15;
+  const int vrow = 4 * g + (i16 >> 2);                  // + 32kb + 16hh (+8)
+  const int vcol = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);  // + 4db (16-byte chunk)
+  const int vhalf = (i16 & 1) * 8;
+  const int vfv = (D == 128) ? 4 * (vrow & 3) : 4 * ((vrow >> 1) & 1);
 
   const float cexp = a.scale_log2e;
-  int bi = 0, kt = 0;
-  Blk kd = describe_block(a, kept_block(0));
-  load_tile(kd, 0);
-  store_tile(0);
-  uint64_t vmask = tile_mask(kd, 0);
-  __syncthreads();
+
+  // ---- prologue: NSTAGE-1 tiles in flight
+  uint64_t mring[NSTAGE];
+  bool ering[NSTAGE];
+#pragma unroll
+  for (int i = 0; i < NSTAGE; ++i) {
+    ering[i] = false;
+    mring[i] = 0;
+  }
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i) {
+    if (ibi < nkept) {
+      mring[i] = issue(i);
+      ering[i] = true;
+    }
+  }
 
   int cur = 0;
 #pragma unroll 1
-  while (true) {
-    // advance to the next tile and start its loads
-    const uint64_t cmask = vmask;
-    ++kt;
-    if (kt >= kd.ntiles) {
-      kt = 0;
-      ++bi;
-      if (bi < nkept) kd = describe_block(a, kept_block(bi));
+  while (ering[0]) {
+    // wait for this wave's loads of the current tile, then publish it
+    if constexpr (NSTAGE == 2) {
+      wait_vmcnt<0>();
+    } else if constexpr (NSTAGE == 3) {
+      if (ering[1]) wait_vmcnt<VM_PER_TILE>(); else wait_vmcnt<0>();
+    } else {
+      if (ering[2]) wait_vmcnt<2 * VM_PER_TILE>();
+      else if (ering[1]) wait_vmcnt<VM_PER_TILE>();
+      else wait_vmcnt<0>();
     }
-    const bool more = bi < nkept;
-    if (more) {
-      load_tile(kd, kt);
-      vmask = tile_mask(kd, kt);
+    __syncthreads();
+    // refill the stage freed by the previous tile
+    {
+      const int st = cur == 0 ? NSTAGE - 1 : cur - 1;
+      if (ibi < nkept) {
+        mring[NSTAGE - 1] = issue(st);
+        ering[NSTAGE - 1] = true;
+      } else {
+        ering[NSTAGE - 1] = false;
+      }
     }
 
+    const uint64_t cmask = mring[0];
     if (wave_active) {
-      const __bf16* ks = Ks[cur];
-      const __bf16* vt = Vt[cur];
+      const unsigned char* ks = kst + cur * TILE_BYTES;
+      const unsigned char* vs = vst + cur * TILE_BYTES;
       f32x16 s[QB][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
-        const int key = 32 * kb + l32;
+        const unsigned char* krow = ks + (32 * kb + l32) * (CPR * 16);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
-          const int chunk = 2 * c + g;
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + key * D + ((chunk ^ (key & KSWZ)) * 8));
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + (((2 * c + g) ^ kswz) * 16));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[qb][c], s[qb][kb], 0, 0, 0);
@@ -349,24 +380,29 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
       }
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + l32;
-        const int swz = (d ^ (d >> 3)) & 7;
+        const int chunk = (4 * db + vcol) ^ vfv;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int pc = 4 * kb + 2 * hh + g;
-            const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vt + d * KT + ((pc ^ swz) * 8));
+            const int row0 = 32 * kb + 16 * hh + vrow;
+            const unsigned char* p0 = vs + row0 * (CPR * 16) + chunk * 16 + vhalf;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * CPR * 16));
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[qb][kb][hh], oacc[qb][db], 0, 0, 0);
           }
       }
     }
-    if (!more) break;
-    store_tile(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
+    // rotate the ring
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i) {
+      mring[i] = mring[i + 1];
+      ering[i] = ering[i + 1];
+    }
+    cur = cur + 1 == NSTAGE ? 0 : cur + 1;
   }
 
   // ---- normalise and store in raster order
@@ -389,11 +425,22 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
   }
 }
 
-template <int D, int NW, int QB, int VCAP>
+template <int D, int NW, int QB, int NSTAGE>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
-  dim3 grid((int64_t)a.B * a.Hh * a.nq * a.tiles);
-  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, VCAP>), grid, dim3(NW * 64), 0, stream, a,
+  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.V * 8;
+  if (lds > 65536) {
+    static bool raised = false;  // benign race: the attribute call is idempotent
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * a.tiles;
+  dim3 grid((unsigned)((nwg + 7) / 8 * 8));
+  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE>), grid, dim3(NW * 64), lds, stream, a,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();
 }
@@ -403,9 +450,9 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                              const int32_t* sel, void* o, hipStream_t stream) {
   if (a.D == 128) {
-    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 64>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, VSA_MAX_CUBE_VOLUME>(a, q, k, v, sel, o, stream);
+    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 1, 3>(a, q, k, v, sel, o, stream);
   }
-  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 64>(a, q, k, v, sel, o, stream);
-  return launch<64, 8, 1, VSA_MAX_CUBE_VOLUME>(a, q, k, v, sel, o, stream);
+  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2>(a, q, k, v, sel, o, stream);
+  return launch<64, 8, 1, 3>(a, q, k, v, sel, o, stream);
 }

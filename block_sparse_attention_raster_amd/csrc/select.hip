@@ -23,7 +23,6 @@ namespace {
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kColChunk = 64;   // cubes scored per LDS stage
-constexpr int VSA_SELECT_ROWS_PER_THREAD = VSA_SELECT_MAX_ROWS / kSelWaves;
 
 __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 #pragma unroll
@@ -34,63 +33,71 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
   return x;
 }
 
-template <int D>
+template <int D, int R>
 __global__ __launch_bounds__(kSelThreads) void vsa_score_topk_kernel(VsaArgs a, const float* __restrict__ qbar,
                                                                      const float* __restrict__ kbar,
                                                                      int32_t* __restrict__ sel) {
+  constexpr int DG = D / 4;                          // float4 groups per row
+  constexpr int RPT = R / kSelWaves;                 // rows per thread
+  constexpr int LPT = kColChunk * DG / kSelThreads;  // float4 loads per thread per chunk
+  static_assert(R % kSelWaves == 0 && (kColChunk * DG) % kSelThreads == 0, "bad tiling");
   extern __shared__ __align__(16) unsigned char smem[];
-  const int R = a.select_rows;
-  float* qs = reinterpret_cast<float*>(smem);                        // [R][D]
-  float* ks = qs + R * D;                                            // [kColChunk][D + 1]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ks + kColChunk * (D + 1));  // [waves][256]
-  uint32_t* sc = hist + kSelWaves * 256;                             // [R][nb]
+  f32x4* qs = reinterpret_cast<f32x4*>(smem);                 // [R][DG]
+  f32x4* ks = qs + R * DG;                                   // [DG][kColChunk], column swizzled
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ks + DG * kColChunk);  // [waves][256]
+  uint32_t* sc = hist + kSelWaves * 256;                     // [R][nb]
 
   const int groups = (a.nq + R - 1) / R;
   const int bh = blockIdx.x / groups;
   const int row0 = (blockIdx.x - bh * groups) * R;
   const int nrows = min(R, a.nq - row0);
-  const float* qsrc = qbar + ((int64_t)bh * a.nq + row0) * D;
-  const float* ksrc = kbar + (int64_t)bh * a.nb * D;
+  const f32x4* qsrc = reinterpret_cast<const f32x4*>(qbar + ((int64_t)bh * a.nq + row0) * D);
+  const f32x4* ksrc = reinterpret_cast<const f32x4*>(kbar + (int64_t)bh * a.nb * D);
   const int tid = threadIdx.x;
 
-  for (int i = tid; i < R * D; i += kSelThreads) qs[i] = (i < nrows * D) ? qsrc[i] : 0.f;
+  for (int i = tid; i < R * DG; i += kSelThreads) qs[i] = (i < nrows * DG) ? qsrc[i] : f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- scores: thread (rg, col) computes rows rg, rg+4, ... for one cube
+  // ---- scores: thread (rg, col) computes rows rg*RPT .. rg*RPT+RPT-1 of one cube per chunk
   const int col = tid & (kColChunk - 1);
   const int rg = tid / kColChunk;
+  f32x4 kreg[LPT];
+  auto load_chunk = [&](int j0) {
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int i = tid + m * kSelThreads;
+      const int dg = i % DG, j = i / DG;
+      kreg[m] = (j0 + j < a.nb) ? ksrc[(int64_t)(j0 + j) * DG + dg] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_chunk(0);
   for (int j0 = 0; j0 < a.nb; j0 += kColChunk) {
     __syncthreads();
-    const int ncols = min(kColChunk, a.nb - j0);
-    for (int i = tid; i < kColChunk * D; i += kSelThreads) {
-      const int j = i / D, d = i - j * D;
-      ks[j * (D + 1) + d] = (j < ncols) ? ksrc[(int64_t)(j0 + j) * D + d] : 0.f;
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int i = tid + m * kSelThreads;
+      const int dg = i % DG, j = i / DG;
+      ks[dg * kColChunk + (j ^ (dg & 15))] = kreg[m];
     }
     __syncthreads();
-    float acc[VSA_SELECT_ROWS_PER_THREAD];
+    if (j0 + kColChunk < a.nb) load_chunk(j0 + kColChunk);
+    float acc[RPT];
 #pragma unroll
-    for (int i = 0; i < VSA_SELECT_ROWS_PER_THREAD; ++i) acc[i] = 0.f;
-    const float* kc = ks + col * (D + 1);
-#pragma unroll 4
-    for (int d = 0; d < D; d += 4) {
-      const float k0 = kc[d], k1 = kc[d + 1], k2 = kc[d + 2], k3 = kc[d + 3];
+    for (int i = 0; i < RPT; ++i) acc[i] = 0.f;
+#pragma unroll 8
+    for (int dg = 0; dg < DG; ++dg) {
+      const f32x4 kv = ks[dg * kColChunk + (col ^ (dg & 15))];
 #pragma unroll
-      for (int i = 0; i < VSA_SELECT_ROWS_PER_THREAD; ++i) {
-        const int r = rg + kSelWaves * i;
-        if (r < R) {
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + r * D + d);
-          acc[i] = fmaf(qv[0], k0, acc[i]);
-          acc[i] = fmaf(qv[1], k1, acc[i]);
-          acc[i] = fmaf(qv[2], k2, acc[i]);
-          acc[i] = fmaf(qv[3], k3, acc[i]);
-        }
+      for (int i = 0; i < RPT; ++i) {
+        const f32x4 qv = qs[(rg * RPT + i) * DG + dg];
+        acc[i] = fmaf(qv[0], kv[0], acc[i]);
+        acc[i] = fmaf(qv[1], kv[1], acc[i]);
+        acc[i] = fmaf(qv[2], kv[2], acc[i]);
+        acc[i] = fmaf(qv[3], kv[3], acc[i]);
       }
     }
-    if (col < ncols) {
+    if (j0 + col < a.nb) {
 #pragma unroll
-      for (int i = 0; i < VSA_SELECT_ROWS_PER_THREAD; ++i) {
-        const int r = rg + kSelWaves * i;
-        if (r < R) sc[r * a.nb + j0 + col] = orderable_key(acc[i]);
-      }
+      for (int i = 0; i < RPT; ++i) sc[(rg * RPT + i) * a.nb + j0 + col] = orderable_key(acc[i]);
     }
   }
   __syncthreads();
@@ -166,34 +173,43 @@ __global__ __launch_bounds__(kSelThreads) void vsa_score_topk_kernel(VsaArgs a, 
 }  // namespace
 
 size_t vsa_select_lds_bytes(const VsaArgs& a) {
-  return (size_t)a.select_rows * a.D * 4 + (size_t)kColChunk * (a.D + 1) * 4 +
-         (size_t)kSelWaves * 256 * 4 + (size_t)a.select_rows * a.nb * 4;
+  return (size_t)a.select_rows * a.D * 4 + (size_t)kColChunk * a.D * 4 + (size_t)kSelWaves * 256 * 4 +
+         (size_t)a.select_rows * a.nb * 4;
 }
 
-// Lets the score/top-k kernels take more than 64 KiB of dynamic LDS.
-hipError_t vsa_prepare_select(size_t lds_bytes) {
+namespace {
+
+template <int D, int R>
+hipError_t launch_rows(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel, size_t lds,
+                       hipStream_t stream) {
   static std::atomic<int> raised{0};
-  if (lds_bytes <= 65536 || raised.load(std::memory_order_acquire)) return hipSuccess;
-  const int cap = 160 * 1024;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vsa_score_topk_kernel<128>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vsa_score_topk_kernel<64>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-  if (e == hipSuccess) raised.store(1, std::memory_order_release);
-  return e;
+  if (lds > 65536 && !raised.load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vsa_score_topk_kernel<D, R>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    raised.store(1, std::memory_order_release);
+  }
+  const int groups = (a.nq + R - 1) / R;
+  hipLaunchKernelGGL((vsa_score_topk_kernel<D, R>), dim3(groups * a.B * a.Hh), dim3(kSelThreads), lds, stream,
+                     a, qbar, kbar, sel);
+  return hipGetLastError();
 }
+
+template <int D>
+hipError_t launch_d(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel, size_t lds,
+                    hipStream_t stream) {
+  switch (a.select_rows) {
+    case 4: return launch_rows<D, 4>(a, qbar, kbar, sel, lds, stream);
+    case 8: return launch_rows<D, 8>(a, qbar, kbar, sel, lds, stream);
+    case 16: return launch_rows<D, 16>(a, qbar, kbar, sel, lds, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
 
 hipError_t vsa_launch_score_topk(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel,
                                  hipStream_t stream) {
-  const int groups = (a.nq + a.select_rows - 1) / a.select_rows;
-  dim3 grid(groups * a.B * a.Hh);
   const size_t lds = vsa_select_lds_bytes(a);
-  if (a.D == 128)
-    hipLaunchKernelGGL(vsa_score_topk_kernel<128>, grid, dim3(kSelThreads), lds, stream, a, qbar, kbar,
-                       sel);
-  else
-    hipLaunchKernelGGL(vsa_score_topk_kernel<64>, grid, dim3(kSelThreads), lds, stream, a, qbar, kbar,
-                       sel);
-  return hipGetLastError();
+  return a.D == 128 ? launch_d<128>(a, qbar, kbar, sel, lds, stream) : launch_d<64>(a, qbar, kbar, sel, lds, stream);
 }

@@ -36,6 +36,8 @@ struct VsaArgs {
   float scale_log2e;     // head_dim^-1/2 * log2(e)
   int32_t select_rows;   // query blocks per score/top-k workgroup
   int32_t tiles;         // query row tiles per query block
+  uint64_t magic_nW;     // ceil(2^32 / nW): floor(x / nW) = (x * magic) >> 32 for x < 2^16
+  uint64_t magic_nH;     // ceil(2^32 / nH)
 };
 
 // Valid region of one block: first token row, extents of the (tt, hh, ww)
