@@ -43,8 +43,9 @@
 // key0 + i/4 at head-dim column base + 4*(i%4) and lane j receives the four
 // keys key0..key0+3 of column base + j. Every lane owns one query row: row max
 // and sum need one exchange between the lane halves and rescaling O is a
-// per-lane scalar. Softmax runs in base 2 on unscaled scores:
-// p = 2^(s*c - m*c) with c = head_dim^-1/2 * log2(e), the same softmax.
+// per-lane scalar. Softmax runs in base 2: p = 2^(s*c - m) with
+// c = head_dim^-1/2 * log2(e) and m a running bound of the scaled row max,
+// the same softmax.
 
 #include "vsa_device.h"
 #include "vsa_limits.h"
@@ -57,10 +58,20 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
-  const __bf16 a = (__bf16)x, b = (__bf16)y;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
+
+// Lazy rescaling of the running softmax state: the row max used in the
+// exponent is raised only when a tile's max exceeds it by more than this many
+// powers of two, so p = 2^(s*c - m) stays below 2^8 and the O / l rescale is
+// skipped on most tiles. The result is the same softmax (both O and l carry
+// the same factor).
+constexpr float kRescaleLog2 = 8.f;
 
 // floor(x / d) for x, d < 2^16 with m = ceil(2^32 / d) (m = 2^32 for d = 1).
 __device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
@@ -108,6 +119,35 @@ __device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk) {
   d.prefix = false;
   d.full = (et == a.ct) & (eh == a.ch) & (ew == a.cw);
   return d;
+}
+
+// Eight ds_read_b64_tr_b16 at rows +0, +8, ..., +56 of a tile with ROWB-byte
+// rows, then a wait for them in the same block (the compiler cannot see these
+// LDS reads, so they must complete before their registers are used). The
+// outputs are early-clobber: a read returns while later reads of the block
+// still need the address register.
+// Transposed reads through the builtin would make the compiler wait for every
+// in-flight global-to-LDS load first, since it cannot tell them apart.
+template <int ROWB>
+__device__ __forceinline__ void tr_read8(uint32_t addr, u32x2 (&r)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%c9\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%c10\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:%c11\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%c12\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:%c13\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:%c14\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:%c15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(addr), "i"(8 * ROWB), "i"(16 * ROWB), "i"(24 * ROWB), "i"(32 * ROWB), "i"(40 * ROWB),
+        "i"(48 * ROWB), "i"(56 * ROWB)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)((const __attribute__((address_space(3))) unsigned char*)p);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -203,6 +243,10 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
       for (int c = 0; c < D / 16; ++c) qreg[qb][c] = bf16x8{};
     }
   }
+  // Q must be resident before the tile loads start: inside the loop the
+  // compiler cannot count how many later loads follow it and would otherwise
+  // wait for all of them before every tile.
+  wait_vmcnt<0>();
   bool wave_active = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) wave_active |= qrow[qb] >= 0;
@@ -229,27 +273,65 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
   int ibi = 0, ikt = 0;
   Blk kd = describe_block(a, kept_block(0));
 
+  // Per-thread parts of this thread's load addresses. Thread (wave, lane)
+  // loads 16-byte unit s*64 + lane of each tile for s = wave*SPW + j, i.e.
+  // key row key_j, chunk position cp_j. When every 64-slot tile of a full
+  // cube is one (hh, ww) cross-section (ch*cw == 64) or the whole cube
+  // (V == 64), tile t's key rows are t*H*W + rel(key) past the cube's first
+  // row, so the byte offsets can be formed once here. Prefix tiles are rows
+  // base + t*64 + key.
+  const bool fastshape = (a.ch * a.cw == KT) || (a.V == KT);
+  uint32_t koff[SPW], voff[SPW], kpoff[SPW], vpoff[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int p = (wave * SPW + j) * 64 + lane;
+    const int key = p / CPR, cp = p % CPR;
+    const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+    const uint32_t rel = (fastshape && key < a.V) ? (uint32_t)srel[key] : 0u;
+    koff[j] = (rel * (uint32_t)a.sn + (uint32_t)((cp ^ (key & KSWZ)) * 8)) * 2u;
+    voff[j] = (rel * (uint32_t)a.sn + (uint32_t)((cp ^ fv) * 8)) * 2u;
+    kpoff[j] = ((uint32_t)key * (uint32_t)a.sn + (uint32_t)((cp ^ (key & KSWZ)) * 8)) * 2u;
+    vpoff[j] = ((uint32_t)key * (uint32_t)a.sn + (uint32_t)((cp ^ fv) * 8)) * 2u;
+  }
+  const int64_t hw = (int64_t)a.H * a.W;
+
   // Issues the loads of the walker's current tile into `stage` and returns
   // its validity mask (bit i: slot i of the tile is valid); then advances.
   auto issue = [&](int stage) -> uint64_t {
     const int t = ikt;
     unsigned char* kdst = kst + stage * TILE_BYTES;
     unsigned char* vdst = vst + stage * TILE_BYTES;
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int s = wave * SPW + j;
-      const int p = s * 64 + lane;
-      const int key = p / CPR, cp = p % CPR;
-      int row = slot_row(kd, t * KT + key);
-      row = row < 0 ? kd.base : row;
-      const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-      const __bf16* ksrc = kh + (int64_t)row * a.sn + ((cp ^ (key & KSWZ)) * 8);
-      const __bf16* vsrc = vh + (int64_t)row * a.sn + ((cp ^ fv) * 8);
-      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + s * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + s * 1024), 16, 0, 0);
-    }
     uint64_t m = ~0ull;
-    if (!(kd.full && (t + 1) * KT <= a.V)) m = __ballot(slot_row(kd, t * KT + lane) >= 0);
+    const bool fullt = kd.full && (t + 1) * KT <= a.V;
+    if (fullt && (kd.prefix || fastshape)) {
+      const int64_t row0 = kd.prefix ? (int64_t)kd.base + (int64_t)t * KT : (int64_t)kd.base + (int64_t)t * hw;
+      const unsigned char* kb = reinterpret_cast<const unsigned char*>(kh + row0 * a.sn);
+      const unsigned char* vb = reinterpret_cast<const unsigned char*>(vh + row0 * a.sn);
+      const uint32_t psel = kd.prefix ? ~0u : 0u;  // select by value, not by address
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int s = wave * SPW + j;
+        const uint32_t ko = (koff[j] & ~psel) | (kpoff[j] & psel);
+        const uint32_t vo = (voff[j] & ~psel) | (vpoff[j] & psel);
+        __builtin_amdgcn_global_load_lds(kb + ko, (lds_void*)(kdst + s * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + vo, (lds_void*)(vdst + s * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int s = wave * SPW + j;
+        const int p = s * 64 + lane;
+        const int key = p / CPR, cp = p % CPR;
+        int row = slot_row(kd, t * KT + key);
+        row = row < 0 ? kd.base : row;
+        const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+        const __bf16* ksrc = kh + (int64_t)row * a.sn + ((cp ^ (key & KSWZ)) * 8);
+        const __bf16* vsrc = vh + (int64_t)row * a.sn + ((cp ^ fv) * 8);
+        __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + s * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + s * 1024), 16, 0, 0);
+      }
+      if (!fullt) m = __ballot(slot_row(kd, t * KT + lane) >= 0);
+    }
     ++ikt;
     if (ikt >= kd.ntiles) {
       ikt = 0;
@@ -298,7 +380,12 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
       else if (ering[1]) wait_vmcnt<VM_PER_TILE>();
       else wait_vmcnt<0>();
     }
-    __syncthreads();
+    // Publish the tile: every wave has waited for its own loads of it and
+    // has finished reading the stage refilled next. A plain s_barrier is
+    // enough; __syncthreads would also wait for the tiles still in flight.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     // refill the stage freed by the previous tile
     {
       const int st = cur == 0 ? NSTAGE - 1 : cur - 1;
@@ -328,6 +415,11 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
             s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[qb][c], s[qb][kb], 0, 0, 0);
         }
       }
+      // V^T operands of this tile (rows 32kb + 16hh + {0, 8} + vrow)
+      u32x2 vr[D / 32][8];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        tr_read8<CPR * 16>(lds_addr(vs + vrow * (CPR * 16) + ((4 * db + vcol) ^ vfv) * 16 + vhalf), vr[db]);
       if (cmask != ~0ull) {
         const uint64_t mg = cmask >> (4 * g);
         const uint32_t m0 = (uint32_t)mg, m1 = (uint32_t)(mg >> 32);
@@ -350,10 +442,16 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrow[qb], mx);
-        const float alpha = __builtin_amdgcn_exp2f((mrow[qb] - mnew) * cexp);
-        const float mc = mnew * cexp;
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cexp;
+        if (__ballot(mx > mrow[qb] + kRescaleLog2) != 0) {
+          const float mnew = fmaxf(mrow[qb], mx);
+          const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - mnew);
+          lrow[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+          mrow[qb] = mnew;
+        }
+        const float mc = mrow[qb];
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -363,10 +461,7 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
             s[qb][kb][r] = p;
             psum += p;
           }
-        lrow[qb] = lrow[qb] * alpha + psum;
-        mrow[qb] = mnew;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+        lrow[qb] += psum;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -379,22 +474,18 @@ __global__ __launch_bounds__(NW * 64) void vsa_attend_kernel(VsaArgs a, const __
           }
       }
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int chunk = (4 * db + vcol) ^ vfv;
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int row0 = 32 * kb + 16 * hh + vrow;
-            const unsigned char* p0 = vs + row0 * (CPR * 16) + chunk * 16 + vhalf;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * CPR * 16));
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const u32x4 w = {vr[db][4 * kb + 2 * hh][0], vr[db][4 * kb + 2 * hh][1],
+                             vr[db][4 * kb + 2 * hh + 1][0], vr[db][4 * kb + 2 * hh + 1][1]};
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[qb][kb][hh], oacc[qb][db], 0, 0, 0);
           }
-      }
     }
     // rotate the ring
 #pragma unroll
