@@ -50,5 +50,5 @@ def test_transposed_read_blocks_keep_their_address(tmp_path):
 @pytest.mark.parametrize("src", ["attend.hip", "select.hip", "pool.hip"])
 def test_kernels_do_not_spill(src, tmp_path):
     asm = _device_asm(src, tmp_path)
-    sizes = re.findall(r"\.private_segment_fixed_size (\d+)", asm)
+    sizes = re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", asm)
     assert sizes and all(int(s) == 0 for s in sizes), sizes
