@@ -9,7 +9,7 @@
 
 enum {
   VSA_ATTEND_ROWS64 = 1,   /* 64 query rows per workgroup (cubes <= 64 tokens) */
-  VSA_ATTEND_ROWS256 = 2   /* 256 query slots per workgroup                    */
+  VSA_ATTEND_ROWS256 = 2   /* 256 query slots per workgroup (8 waves)          */
 };
 
 #endif
