@@ -102,9 +102,13 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   // Score/top-k tiling: rows of the per-row score buffer live in LDS
   // (4 bytes per cube and row); keep it within the budget and prefer enough
   // workgroups to cover the machine.
+  // Up to VSA_SELECT_MFMA_MAX_BLOCKS cubes the matrix-core kernel takes 16
+  // rows per workgroup.
   int rows = VSA_SELECT_MAX_ROWS;
-  while (rows > 1 && (int64_t)rows * nb * 4 > VSA_SELECT_SCORE_LDS) rows /= 2;
-  while (rows > 4 && BH * ceil_div(nq, rows) < 1024) rows /= 2;
+  if (nb > VSA_SELECT_MFMA_MAX_BLOCKS) {
+    while (rows > 1 && (int64_t)rows * nb * 4 > VSA_SELECT_SCORE_LDS) rows /= 2;
+    while (rows > 4 && BH * ceil_div(nq, rows) < 1024) rows /= 2;
+  }
   r.select_rows = rows;
 
   // Attention tiling: query rows per workgroup by cube volume.

@@ -84,6 +84,13 @@ def test_small_case_full_oracle(case):
     _full_check(w, topk)
 
 
+def test_many_cubes_vector_select_path():
+    """More than 2048 cubes: selection runs on the vector-FMA kernel."""
+    w = synthetic.custom_workload("many_cubes", seed=12, batch=1, heads=2, head_dim=64,
+                                  latent=(16, 24, 48), cube=(2, 2, 2), topk=16)
+    _full_check(w, 16, blocks_per_head=10)
+
+
 def test_all_blocks_equals_dense_attention():
     """topk == num_blocks: the sparse path must give dense attention."""
     import torch
