@@ -9,16 +9,16 @@
 // in tiles of 64 key slots.
 //
 // Index map (fastbsa package page, section "How it works": the raster to
-// block map is evaluated inside the kernel). A block's V = ct*ch*cw slots are
-// numbered s = (tt*ch + hh)*cw + ww. At start-up the workgroup tabulates,
-// for every slot, its row offset (tt*H + hh)*W + ww from the cube's first
-// token and its packed (tt, hh, ww); afterwards a slot's token row is one LDS
-// read plus an add. A slot is valid when (tt, hh, ww) lies inside the
-// block's valid extents (partial cubes at the far edge of an axis); prefix
-// block slots are rows p*V + s, valid below the prefix length. Invalid key
-// slots load the block's first row (finite data) and are masked to -inf, so
-// only tiles of partial blocks pay for masking; a block's tiles stop at its
-// last valid slot.
+// block map is evaluated inside the kernel). The n valid tokens of a block
+// are numbered k = (tt*eh + hh)*ew + ww over its valid extents (et, eh, ew)
+// (partial cubes at the far edge of an axis have smaller extents); prefix
+// block tokens are rows p*V + k. Both query rows and key tiles walk this
+// compact numbering, so a block of n tokens fills floor(n/64) whole key
+// tiles and at most one tail tile, whose slots past n load the block's first
+// row (finite data) and are masked to -inf. For whole cubes the workgroup
+// tabulates each k's row offset (tt*H + hh)*W + ww from the cube's first
+// token at start-up (one LDS read per row); partial cubes unravel k with
+// multiply-high divisions by eh*ew and ew.
 //
 // Data movement. K and V tiles go from HBM straight into LDS with 16-byte
 // global_load_lds (no registers), NSTAGE tiles deep; each wave issues its
@@ -47,6 +47,8 @@
 // c = head_dim^-1/2 * log2(e) and m a running bound of the scaled row max,
 // the same softmax.
 
+#include <type_traits>
+
 #include "vsa_device.h"
 #include "vsa_limits.h"
 
@@ -65,6 +67,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
 
+// The values of x held by lanes l % 32 and 32 + l % 32 (the two halves of a
+// query row's keys), in every lane l: one v_permlane32_swap, which exchanges
+// the upper half of its first operand with the lower half of its second.
+__device__ __forceinline__ f32x2 halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // Lazy rescaling of the running softmax state: the row max used in the
 // exponent is raised only when a tile's max exceeds it by more than this many
 // powers of two, so p = 2^(s*c - m) stays below 2^8 and the O / l rescale is
@@ -77,20 +87,15 @@ __device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
   return (int32_t)(((uint64_t)(uint32_t)x * m) >> 32);
 }
 
-// Packed slot coordinates: tt | hh << 10 | ww << 20 (each < 1024).
-__device__ __forceinline__ bool slot_valid(uint32_t crd, uint32_t ext) {
-  return ((crd & 1023u) < (ext & 1023u)) & (((crd >> 10) & 1023u) < ((ext >> 10) & 1023u)) &
-         ((crd >> 20) < (ext >> 20));
-}
-
-// Valid region of a kept or query block in slot space.
+// Valid region of a kept or query block.
 struct Blk {
-  int32_t base;     // first token row (the row of slot 0, always valid)
-  uint32_t ext;     // packed valid extents (et, eh, ew); prefix blocks (1, 1, n)
-  int32_t last;     // last valid slot
-  int32_t ntiles;   // key tiles up to the last valid slot
+  int32_t base;     // first token row (the row of index 0)
+  int32_t n;        // valid tokens
+  int32_t ntiles;   // key tiles of the compact numbering
+  int32_t ew, ehw;  // partial cubes: valid extents ew and eh*ew
+  uint64_t mw, mhw; // and their division magics
   bool prefix;
-  bool full;        // every slot below V valid
+  bool full;        // a whole cube (n == V) or a whole prefix block
 };
 
 __device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk, int32_t kt) {
@@ -99,9 +104,11 @@ __device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk, int
     const int32_t s = blk * a.V;
     const int32_t n = min(a.V, a.P - s);
     d.base = s;
-    d.ext = 1u | (1u << 10) | ((uint32_t)n << 20);
-    d.last = n - 1;
+    d.n = n;
     d.ntiles = (n + kt - 1) / kt;
+    d.ew = n;
+    d.ehw = n;
+    d.mw = d.mhw = 0;
     d.prefix = true;
     d.full = n == a.V;
     return d;
@@ -113,51 +120,30 @@ __device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk, int
   const int32_t bh = rest - bt * a.nH;
   const int32_t t0 = bt * a.ct, h0 = bh * a.ch, w0 = bw * a.cw;
   const int32_t et = min(a.ct, a.T - t0), eh = min(a.ch, a.H - h0), ew = min(a.cw, a.W - w0);
+  const int ih = eh != a.ch, iw = ew != a.cw;
   d.base = a.P + (t0 * a.H + h0) * a.W + w0;
-  d.ext = (uint32_t)et | ((uint32_t)eh << 10) | ((uint32_t)ew << 20);
-  d.last = ((et - 1) * a.ch + (eh - 1)) * a.cw + (ew - 1);
-  d.ntiles = d.last / kt + 1;
+  d.n = et * eh * ew;
+  d.ntiles = (d.n + kt - 1) / kt;
+  d.ew = ew;
+  d.ehw = eh * ew;
+  d.mw = a.magic_ew[iw];
+  d.mhw = a.magic_ehw[2 * ih + iw];
   d.prefix = false;
-  d.full = (et == a.ct) & (eh == a.ch) & (ew == a.cw);
+  d.full = d.n == a.V;
   return d;
 }
 
-// NR ds_read_b64_tr_b16 (NR = 4 or 8) at rows +0, +8, +16, ... of a tile
-// with ROWB-byte rows, then a wait for them in the same block (the compiler
-// cannot see these LDS reads, so they must complete before their registers
-// are used). The outputs are early-clobber: a read returns while later reads
-// of the block still need the address register. Transposed reads through the
-// builtin would make the compiler wait for every in-flight global-to-LDS load
-// first, since it cannot tell them apart.
-template <int ROWB, int NR>
-__device__ __forceinline__ void tr_read(uint32_t addr, u32x2 (&r)[NR]) {
-  static_assert(NR == 4 || NR == 8, "4 or 8 transposed reads");
-  if constexpr (NR == 8) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%c9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:%c10\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:%c11\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:%c12\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:%c13\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:%c14\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:%c15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(addr), "i"(8 * ROWB), "i"(16 * ROWB), "i"(24 * ROWB), "i"(32 * ROWB), "i"(40 * ROWB),
-          "i"(48 * ROWB), "i"(56 * ROWB)
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %4 offset:%c5\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:%c6\n\t"
-        "ds_read_b64_tr_b16 %3, %4 offset:%c7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(addr), "i"(8 * ROWB), "i"(16 * ROWB), "i"(24 * ROWB)
-        : "memory");
-  }
+// 16-byte global-to-LDS copies (global_load_lds_dwordx4: lane l's 16 bytes
+// land at M0 + 16*l). Written as asm so that the compiler, which cannot tell
+// these LDS writes apart from the kernel's LDS reads, does not make every LDS
+// read wait for all copies in flight; the kernel orders them itself with
+// explicit vmcnt waits and barriers. The compiler sets M0 from the input
+// operand. No register outputs: nothing is written to VGPRs.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16(const void* addr, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -171,7 +157,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
                                                              const __bf16* __restrict__ k,
@@ -190,13 +176,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;
   static_assert(SLABS % NW == 0 && SPW >= 1, "tile loads must split evenly over the waves");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
+  static_assert(!PIPE || NSTAGE >= 3, "the pipelined loop keeps two tiles in use");
   constexpr int VM_PER_TILE = 2 * SPW;   // vector-memory instructions per wave per tile
 
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* kst = smem;                              // [NSTAGE][TILE_BYTES]
   unsigned char* vst = smem + NSTAGE * TILE_BYTES;        // [NSTAGE][TILE_BYTES]
   int32_t* srel = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);  // [V]
-  uint32_t* scrd = reinterpret_cast<uint32_t*>(srel + a.V);                   // [V]
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
   // id is remapped to give each XCD a contiguous range of (head, block) work.
@@ -212,7 +198,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int b = bh / a.Hh, h = bh - b * a.Hh;
   const Blk qd = describe_block(a, qblk, KT);
   const int slot0 = tile * RW;
-  if (slot0 > qd.last) return;
+  if (slot0 >= qd.n) return;
 
   const int tid = threadIdx.x;
   {
@@ -223,7 +209,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const int hh = rem / a.cw;
       const int ww = rem - hh * a.cw;
       srel[s] = (tt * a.H + hh) * a.W + ww;
-      scrd[s] = (uint32_t)tt | ((uint32_t)hh << 10) | ((uint32_t)ww << 20);
     }
   }
   __syncthreads();
@@ -235,15 +220,18 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   __bf16* oh = o + (int64_t)b * a.osb + (int64_t)h * a.osh;
   const int32_t* selrow = sel + ((int64_t)bh * a.nq + qblk) * a.topk;
 
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // token row of slot s of block d, or -1 when the slot is not valid
-  auto slot_row = [&](const Blk& d, int s) -> int {
-    if (s >= a.V) return -1;
-    const uint32_t crd = d.prefix ? ((uint32_t)s << 20) : scrd[s];
-    if (!slot_valid(crd, d.ext)) return -1;
-    return d.base + (d.prefix ? s : srel[s]);
+  // token row of compact index k < d.n of block d
+  auto compact_row = [&](const Blk& d, int k) -> int {
+    if (d.prefix) return d.base + k;
+    if (d.full) return d.base + srel[k];
+    const int tt = fast_div(k, d.mhw);
+    const int r = k - tt * d.ehw;
+    const int hh = fast_div(r, d.mw);
+    const int ww = r - hh * d.ew;
+    return d.base + (tt * a.H + hh) * a.W + ww;
   };
 
   // ---- Q rows of this wave, in MFMA B-operand layout
@@ -251,7 +239,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   bf16x8 qreg[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = slot_row(qd, slot0 + wave * 32 * QB + qb * 32 + l32);
+    const int slot = slot0 + wave * 32 * QB + qb * 32 + l32;
+    qrow[qb] = slot < qd.n ? compact_row(qd, slot) : -1;
     if (qrow[qb] >= 0) {
       const __bf16* src = qh + (int64_t)qrow[qb] * a.sn + 8 * g;
 #pragma unroll
@@ -291,73 +280,33 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   int ibi = 0, ikt = 0;
   Blk kd = describe_block(a, kept_block(0), KT);
 
-  // Per-thread parts of this thread's load addresses. Thread (wave, lane)
-  // loads 16-byte unit s*64 + lane of each tile for s = wave*SPW + j, i.e.
-  // key row key_j, chunk position cp_j. When a tile of a full cube is a
-  // whole number of (hh, ww) cross-sections (KT divisible by ch*cw), tile
-  // t's key rows are t*(KT/(ch*cw))*H*W + rel(key) past the cube's first
-  // row, so the byte offsets can be formed once here. Prefix tiles are rows
-  // base + t*KT + key.
-  const int chw = a.ch * a.cw;
-  const bool fastshape = (KT % chw) == 0;
-  uint32_t rowoff[SPW];   // byte offset of this thread's key row j in a fast tile
-#pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int key = ((wave * SPW + j) * 64 + lane) / CPR;
-    const uint32_t rel = (fastshape && key < a.V) ? (uint32_t)srel[key] : 0u;
-    rowoff[j] = rel * (uint32_t)a.sn * 2u;
-  }
-  // byte offsets of this thread's 16-byte K and V chunks inside key row j
-  auto koff_chunk = [&](int j) -> uint32_t {
-    const int p = (wave * SPW + j) * 64 + lane;
-    const int key = p / CPR, cp = p % CPR;
-    return (uint32_t)((cp ^ (key & KSWZ)) * 16);
-  };
-  auto voff_chunk = [&](int j) -> uint32_t {
-    const int p = (wave * SPW + j) * 64 + lane;
-    const int key = p / CPR, cp = p % CPR;
-    const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-    return (uint32_t)((cp ^ fv) * 16);
-  };
-  const int64_t tile_rows = fastshape ? (int64_t)(KT / chw) * a.H * a.W : 0;
-
+  // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
+  // for s = wave*SPW + j: key row (s*64 + lane)/CPR, chunk position
+  // (s*64 + lane)%CPR, XOR-swizzled by key (K: chunk ^ (key & KSWZ); V: see
+  // the transposed reads). The per-lane offsets are recomputed at every
+  // issue from an opaque copy of the lane id, so that they are not kept in
+  // registers across the compute steps.
   // Issues the loads of the walker's current tile into `stage` and returns
   // its validity mask (bit i: slot i of the tile is valid); then advances.
   auto issue = [&](int stage) -> uint64_t {
     const int t = ikt;
     unsigned char* kdst = kst + stage * TILE_BYTES;
     unsigned char* vdst = vst + stage * TILE_BYTES;
-    uint64_t m = FULLM;
-    const bool fullt = kd.full && (t + 1) * KT <= a.V;
-    if (fullt && (kd.prefix || fastshape)) {
-      const int64_t row0 = kd.prefix ? (int64_t)kd.base + (int64_t)t * KT : (int64_t)kd.base + (int64_t)t * tile_rows;
-      const unsigned char* kb = reinterpret_cast<const unsigned char*>(kh + row0 * a.sn);
-      const unsigned char* vb = reinterpret_cast<const unsigned char*>(vh + row0 * a.sn);
+    const int nleft = kd.n - t * KT;          // valid slots from this tile on
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int s = wave * SPW + j;
-        // prefix tiles: key rows are consecutive
-        const uint32_t ro = kd.prefix ? (uint32_t)((s * 64 + lane) / CPR) * (uint32_t)a.sn * 2u : rowoff[j];
-        const uint32_t ko = ro + koff_chunk(j), vo = ro + voff_chunk(j);
-        __builtin_amdgcn_global_load_lds(kb + ko, (lds_void*)(kdst + s * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + vo, (lds_void*)(vdst + s * 1024), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int s = wave * SPW + j;
-        const int p = s * 64 + lane;
-        const int key = p / CPR, cp = p % CPR;
-        int row = slot_row(kd, t * KT + key);
-        row = row < 0 ? kd.base : row;
-        const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-        const __bf16* ksrc = kh + (int64_t)row * a.sn + ((cp ^ (key & KSWZ)) * 8);
-        const __bf16* vsrc = vh + (int64_t)row * a.sn + ((cp ^ fv) * 8);
-        __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(kdst + s * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(vdst + s * 1024), 16, 0, 0);
-      }
-      if (!fullt) m = __ballot(lane < KT && slot_row(kd, t * KT + lane) >= 0);
+    for (int j = 0; j < SPW; ++j) {
+      const int s = wave * SPW + j;
+      const int p = s * 64 + ln;
+      const int key = p / CPR, cp = p % CPR;
+      const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+      const int row = key < nleft ? compact_row(kd, t * KT + key) : kd.base;
+      const uint32_t ro = (uint32_t)row * (uint32_t)a.sn * 2u;
+      dma16(kh, ro + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
+      dma16(vh, ro + (uint32_t)((cp ^ fv) * 16), lds_addr(vdst + s * 1024));
     }
+    const uint64_t m = nleft >= KT ? FULLM : __ballot(lane < nleft);
     ++ikt;
     if (ikt >= kd.ntiles) {
       ikt = 0;
@@ -376,158 +325,364 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int vfv = (D == 128) ? 4 * (vrow & 3) : 4 * ((vrow >> 1) & 1);
 
   const float cexp = a.scale_log2e;
+  constexpr int NC = D / 16;       // 16-wide head-dim steps of S^T = K Q^T
+  constexpr int NVR = 4 * NKB;     // transposed reads per 32-wide head-dim block of P.V
 
-  // ---- prologue: NSTAGE-1 tiles in flight
-  uint64_t mring[NSTAGE];
-  bool ering[NSTAGE];
+  // K operands of the tile in `stage`: lane holds key 32kb + l32, head-dim
+  // values 16c + 8g .. +7.
+  auto kread = [&](int stage, int kb, int c) -> bf16x8 {
+    const unsigned char* krow = kst + stage * TILE_BYTES + (32 * kb + l32) * (CPR * 16);
+    return *reinterpret_cast<const bf16x8*>(krow + (((2 * c + g) ^ kswz) * 16));
+  };
+  // Transposed V reads of head-dim block db: read i covers key rows
+  // 8i + vrow of the tile (32kb + 16hh + 8e for i = 4kb + 2hh + e).
+  auto vread = [&](int stage, int db, int i) -> u32x2 {
+    const unsigned char* base = vst + stage * TILE_BYTES + vrow * (CPR * 16) + ((4 * db + vcol) ^ vfv) * 16 + vhalf;
+    const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * i * (CPR * 16)));
+    return __builtin_bit_cast(u32x2, t);
+  };
+
+  // S^T = K Q^T for the tile in `stage` (keys 32kb + ..., see the header)
+  auto qk = [&](int stage, f32x16 (&sacc)[QB][NKB]) {
+    bf16x8 kop[NKB][NC];
 #pragma unroll
-  for (int i = 0; i < NSTAGE; ++i) {
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kop[kb][c] = kread(stage, kb, c);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][c], qreg[qb][c], sacc[qb][kb], 0, 0, 0);
+    }
+  };
+
+  // O^T += V^T P^T for the tile in `stage`, one head-dim block of 32 at a time
+  auto pv = [&](int stage, const bf16x8 (&pb)[QB][NKB][2]) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      u32x2 vr[NVR];
+#pragma unroll
+      for (int i = 0; i < NVR; ++i) vr[i] = vread(stage, db, i);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const u32x4 w = {vr[4 * kb + 2 * hh][0], vr[4 * kb + 2 * hh][1], vr[4 * kb + 2 * hh + 1][0],
+                           vr[4 * kb + 2 * hh + 1][1]};
+          const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[qb][kb][hh], oacc[qb][db], 0, 0, 0);
+        }
+    }
+  };
+
+  // Masked online softmax of one tile's scores, without branches on the
+  // common path. P goes out as bf16 operands. A row's exponent offset m is
+  // raised only when the tile's scaled max exceeds it by more than
+  // kRescaleLog2; alpha = 2^(m_old - m_new) (1 when unchanged) scales the
+  // row sum here and the O accumulators in `rescale`, after the P.V steps
+  // that still use the old scale. The row sum adds the bf16 P values that
+  // the P.V step multiplies (one v_dot2 per pair).
+  auto softmax = [&](f32x16 (&sacc)[QB][NKB], uint64_t cmask, bool masked, bf16x8 (&pb)[QB][NKB][2],
+                     float (&alpha)[QB]) {
+    if (masked) {
+      const uint64_t mg = cmask >> (4 * g);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t mk = (uint32_t)(mg >> (32 * kb));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int bit = 8 * (r >> 2) + (r & 3);
+          const bool valid = (mk >> bit) & 1u;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sacc[qb][kb][r] = valid ? sacc[qb][kb][r] : -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = sacc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
+      const f32x2 hv = halves(mx);
+      mx = fmaxf(hv[0], hv[1]) * cexp;
+      const float mold = mrow[qb];
+      const float mc = mx > mold + kRescaleLog2 ? mx : mold;
+      alpha[qb] = __builtin_amdgcn_exp2f(mold - mc);
+      mrow[qb] = mc;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 8 * hh + 2 * i;
+            // (a bit_cast of the vector element w[i] would read element 0)
+            const uint32_t pw = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], cexp, -mc)),
+                                            __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r + 1], cexp, -mc)));
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), ones, psum, false);
+            w[i] = pw;
+          }
+          pb[qb][kb][hh] = __builtin_bit_cast(bf16x8, w);
+        }
+      lrow[qb] = fmaf(lrow[qb], alpha[qb], psum);
+    }
+  };
+  auto rescale = [&](const float (&alpha)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (__ballot(alpha[qb] != 1.f) != 0) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha[qb];
+      }
+    }
+  };
+
+  // One pipelined step, QB == 1, in a fixed issue order of 32 (D = 128) or
+  // 16 (D = 64) slots of one MFMA each, fenced so that the compiler keeps
+  // the order: first the QK MFMAs of tile `ks` with the K reads KA slots
+  // ahead and, in the last slots, the first head-dim block's V reads; then
+  // the P.V MFMAs of tile `vs_` (P of the previous step in pb) with the next
+  // block's V reads and, between them, the softmax of the new scores in
+  // small pieces (masking of a tail tile, row max, exponent offset, then
+  // pairs of exponentials packed to bf16). WITH_PV false (the first tile)
+  // keeps the slots without their P.V work.
+  auto step = [&](auto with_pv, auto masked, int ks, int vs_, const bf16x8 (&pb)[QB][NKB][2], uint64_t cmask,
+                  bf16x8 (&pn)[QB][NKB][2], float (&alpha)[QB]) {
+    constexpr bool WITH_PV = decltype(with_pv)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    static_assert(QB == 1, "the fixed schedule is written for one query block per wave");
+    constexpr int KA = 4;                   // K reads ahead of their MFMA
+    constexpr int NQ = NKB * NC;            // QK MFMAs
+    constexpr int NDB = D / 32;             // head-dim blocks of P.V
+    constexpr int PPD = 2 * NKB;            // P.V MFMAs per head-dim block
+    constexpr int NP = NDB * PPD;           // P.V MFMAs
+    constexpr int RPS = NVR / PPD;          // V reads per P.V slot (next block)
+    constexpr int NPAIR = NKB * 8;          // exponential pairs per lane
+    constexpr int P_M0 = 0, P_M1 = (NP >= 16 ? 2 : 1), P_M2 = P_M1 + 1, P_PAIR0 = P_M2 + 1;
+    static_assert(NVR % PPD == 0 && P_PAIR0 < NP, "schedule shape");
+    f32x16 sa[NKB];
+    bf16x8 kop[NQ];
+    u32x2 vr[NDB][NVR];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float mx = 0.f, mc = 0.f, psum = 0.f;
+    // slot r of 32-key block kb holds key 32kb + 8(r/4) + 4g + r%4
+    auto mask_block = [&](int kb) {
+      const uint32_t mk = (uint32_t)((cmask >> (4 * g)) >> (32 * kb));
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sa[kb][r] = ((mk >> (8 * (r >> 2) + (r & 3))) & 1u) ? sa[kb][r] : -INFINITY;
+    };
+#pragma unroll
+    for (int i = 0; i < KA; ++i) kop[i] = kread(ks, i / NC, i % NC);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (q + KA < NQ) kop[q + KA] = kread(ks, (q + KA) / NC, (q + KA) % NC);
+      // first block's V reads, two per slot in the last NVR/2 slots
+      if (WITH_PV && q >= NQ - NVR / 2) {
+        const int i = 2 * (q - (NQ - NVR / 2));
+        vr[0][i] = vread(vs_, 0, i);
+        vr[0][i + 1] = vread(vs_, 0, i + 1);
+      }
+      const int kb = q / NC, c = q % NC;
+      sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[q], qreg[0][c], c == 0 ? f32x16{} : sa[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int db = p / PPD, kb = (p % PPD) / 2, hh = p % 2;
+      if constexpr (WITH_PV) {
+        if (db + 1 < NDB) {
+#pragma unroll
+          for (int e = 0; e < RPS; ++e) vr[db + 1][RPS * (p % PPD) + e] = vread(vs_, db + 1, RPS * (p % PPD) + e);
+        }
+        const u32x4 w = {vr[db][4 * kb + 2 * hh][0], vr[db][4 * kb + 2 * hh][1], vr[db][4 * kb + 2 * hh + 1][0],
+                         vr[db][4 * kb + 2 * hh + 1][1]};
+        oacc[0][db] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[0][kb][hh], oacc[0][db], 0, 0, 0);
+      }
+      // softmax pieces
+      if (p == P_M0) {
+        if constexpr (MASKED) mask_block(0);
+        mx = sa[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[0][r]);
+      }
+      if (p == P_M1) {
+#pragma unroll
+        for (int k2 = 1; k2 < NKB; ++k2) {
+          if constexpr (MASKED) mask_block(k2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[k2][r]);
+        }
+      }
+      if (p == P_M2) {
+        const f32x2 hv = halves(mx);
+        const float m = fmaxf(hv[0], hv[1]) * cexp;
+        const float mold = mrow[0];
+        mc = m > mold + kRescaleLog2 ? m : mold;
+        alpha[0] = __builtin_amdgcn_exp2f(mold - mc);
+        mrow[0] = mc;
+      }
+#pragma unroll
+      for (int k = 0; k < NPAIR; ++k) {
+        if (p == P_PAIR0 + (k * (NP - P_PAIR0)) / NPAIR) {
+          const int pkb = k / 8, phh = (k % 8) / 4, i = k % 4, r = 8 * phh + 2 * i;
+          const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sa[pkb][r], cexp, -mc)),
+                                         __builtin_amdgcn_exp2f(fmaf(sa[pkb][r + 1], cexp, -mc)));
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, psum, false);
+          u32x4 t = __builtin_bit_cast(u32x4, pn[0][pkb][phh]);
+          t[i] = w;
+          pn[0][pkb][phh] = __builtin_bit_cast(bf16x8, t);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lrow[0] = fmaf(lrow[0], alpha[0], psum);
+  };
+
+  // Publish: every wave has waited for its own loads of the tiles needed
+  // next. A plain s_barrier suffices; __syncthreads would also wait for the
+  // tiles still in flight.
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Tile ring: slot i holds the i-th tile from the one the next step starts
+  // with. AHEAD tiles are in flight when a step begins.
+  constexpr int AHEAD = PIPE ? NSTAGE - 2 : NSTAGE - 1;
+  uint64_t mring[AHEAD + 1];
+  bool ering[AHEAD + 1];
+#pragma unroll
+  for (int i = 0; i <= AHEAD; ++i) {
     ering[i] = false;
     mring[i] = 0;
   }
 #pragma unroll
-  for (int i = 0; i < NSTAGE - 1; ++i) {
+  for (int i = 0; i < AHEAD; ++i) {
     if (ibi < nkept) {
       mring[i] = issue(i);
       ering[i] = true;
     }
   }
-
-  int cur = 0;
-#pragma unroll 1
-  while (ering[0]) {
-    // wait for this wave's loads of the current tile, then publish it
-    if constexpr (NSTAGE == 2) {
-      wait_vmcnt<0>();
-    } else if constexpr (NSTAGE == 3) {
-      if (ering[1]) wait_vmcnt<VM_PER_TILE>(); else wait_vmcnt<0>();
-    } else {
+  // wait for this wave's loads of ring slot 0 (later tiles may stay in flight)
+  auto wait_first = [&]() {
+    if constexpr (AHEAD >= 3) {
       if (ering[2]) wait_vmcnt<2 * VM_PER_TILE>();
       else if (ering[1]) wait_vmcnt<VM_PER_TILE>();
       else wait_vmcnt<0>();
+    } else if constexpr (AHEAD == 2) {
+      if (ering[1]) wait_vmcnt<VM_PER_TILE>(); else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
     }
-    // Publish the tile: every wave has waited for its own loads of it and
-    // has finished reading the stage refilled next. A plain s_barrier is
-    // enough; __syncthreads would also wait for the tiles still in flight.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // refill the stage freed by the previous tile
-    {
-      const int st = cur == 0 ? NSTAGE - 1 : cur - 1;
-      if (ibi < nkept) {
-        mring[NSTAGE - 1] = issue(st);
-        ering[NSTAGE - 1] = true;
-      } else {
-        ering[NSTAGE - 1] = false;
-      }
+  };
+  // refill ring slot AHEAD into `stage`, then the ring moves by one
+  auto refill = [&](int stage) {
+    if (ibi < nkept) {
+      mring[AHEAD] = issue(stage);
+      ering[AHEAD] = true;
+    } else {
+      ering[AHEAD] = false;
     }
-
-    const uint64_t cmask = mring[0];
-    if (wave_active) {
-      const unsigned char* ks = kst + cur * TILE_BYTES;
-      const unsigned char* vs = vst + cur * TILE_BYTES;
-      f32x16 s[QB][NKB];
+  };
+  auto shift = [&]() {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
-        const unsigned char* krow = ks + (32 * kb + l32) * (CPR * 16);
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + (((2 * c + g) ^ kswz) * 16));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[qb][c], s[qb][kb], 0, 0, 0);
-        }
-      }
-      // V^T operands of this tile (rows 32kb + 16hh + {0, 8} + vrow)
-      u32x2 vr[D / 32][4 * NKB];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        tr_read<CPR * 16, 4 * NKB>(lds_addr(vs + vrow * (CPR * 16) + ((4 * db + vcol) ^ vfv) * 16 + vhalf),
-                                   vr[db]);
-      if (cmask != FULLM) {
-        const uint64_t mg = cmask >> (4 * g);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const uint32_t mk = (uint32_t)(mg >> (32 * kb));
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int bit = 8 * (r >> 2) + (r & 3);
-            const bool valid = (mk >> bit) & 1u;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = valid ? s[qb][kb][r] : -INFINITY;
-          }
-        }
-      }
-      bf16x8 pb[QB][NKB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = s[qb][0][0];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cexp;
-        if (__ballot(mx > mrow[qb] + kRescaleLog2) != 0) {
-          const float mnew = fmaxf(mrow[qb], mx);
-          const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - mnew);
-          lrow[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
-          mrow[qb] = mnew;
-        }
-        const float mc = mrow[qb];
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], cexp, -mc));
-            s[qb][kb][r] = p;
-            psum += p;
-          }
-        lrow[qb] += psum;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              w[i] = pack_bf16x2(s[qb][kb][8 * hh + 2 * i], s[qb][kb][8 * hh + 2 * i + 1]);
-            pb[qb][kb][hh] = __builtin_bit_cast(bf16x8, w);
-          }
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 w = {vr[db][4 * kb + 2 * hh][0], vr[db][4 * kb + 2 * hh][1],
-                             vr[db][4 * kb + 2 * hh + 1][0], vr[db][4 * kb + 2 * hh + 1][1]};
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[qb][kb][hh], oacc[qb][db], 0, 0, 0);
-          }
-    }
-    // rotate the ring
-#pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i) {
+    for (int i = 0; i < AHEAD; ++i) {
       mring[i] = mring[i + 1];
       ering[i] = ering[i + 1];
     }
-    cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+  };
+
+  if constexpr (PIPE) {
+    // Software pipeline. Tile t sits in stage t % NSTAGE. Step j runs QK of
+    // tile j and the P.V of tile j-1 (whose P the previous step made), with
+    // the softmax of tile j on the vector ALUs while the P.V matrix ops run.
+    // Barrier j publishes tile j; every wave has then finished step j-1, so
+    // tile j-2's stage is free and takes tile j + NSTAGE - 2.
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    bf16x8 pb[QB][NKB][2];
+    // first tile: QK and softmax only (every kept list has a tile)
+    wait_first();
+    barrier();
+    refill(AHEAD);
+    if (wave_active) {
+      float alpha[QB];
+      if (mring[0] == FULLM) step(F_{}, F_{}, 0, 0, pb, mring[0], pb, alpha);
+      else step(F_{}, T_{}, 0, 0, pb, mring[0], pb, alpha);
+      rescale(alpha);
+    }
+    shift();
+    int cur = 1, prev = 0;
+    // steady state; the step after the last tile runs the last P.V only
+#pragma unroll 1
+    while (true) {
+      const bool have = ering[0];
+      if (have) wait_first();
+      barrier();
+      refill(cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD);
+      if (!have) {
+        if (wave_active) pv(prev, pb);
+        break;
+      }
+      if (wave_active) {
+        const uint64_t cm = mring[0];
+        bf16x8 pn[QB][NKB][2];
+        float alpha[QB];
+        if (cm == FULLM) step(T_{}, F_{}, cur, prev, pb, cm, pn, alpha);
+        else step(T_{}, T_{}, cur, prev, pb, cm, pn, alpha);
+        rescale(alpha);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          pb[0][kb][0] = pn[0][kb][0];
+          pb[0][kb][1] = pn[0][kb][1];
+        }
+      }
+      prev = cur;
+      cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+      shift();
+    }
+  } else {
+    int cur = 0;
+#pragma unroll 1
+    while (ering[0]) {
+      wait_first();
+      barrier();
+      // refill the stage freed by the previous tile
+      refill(cur == 0 ? NSTAGE - 1 : cur - 1);
+      if (wave_active) {
+        f32x16 sa[QB][NKB];
+        bf16x8 pb[QB][NKB][2];
+        float alpha[QB];
+        qk(cur, sa);
+        softmax(sa, mring[0], mring[0] != FULLM, pb, alpha);
+        rescale(alpha);
+        pv(cur, pb);
+      }
+      shift();
+      cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+    }
   }
 
   // ---- normalise and store in raster order
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = lrow[qb] + __shfl_xor(lrow[qb], 32, 64);
-    const float inv = 1.f / ltot;
+    const f32x2 hl = halves(lrow[qb]);
+    const float inv = 1.f / (hl[0] + hl[1]);
     if (qrow[qb] >= 0) {
       __bf16* dst = oh + (int64_t)qrow[qb] * a.osn + 4 * g;
 #pragma unroll
@@ -543,15 +698,15 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   }
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
-  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.V * 8;
+  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.V * 4;
   if (lds > 65536) {
     static bool raised = false;  // benign race: the attribute call is idempotent
     if (!raised) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE>),
+          reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE>),
           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
       raised = true;
@@ -559,7 +714,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   }
   const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * a.tiles;
   dim3 grid((unsigned)((nwg + 7) / 8 * 8));
-  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE>), grid, dim3(NW * 64), lds, stream, a,
+  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE>), grid, dim3(NW * 64), lds, stream, a,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();
 }
@@ -573,9 +728,9 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                              const int32_t* sel, void* o, hipStream_t stream) {
   if (a.D == 128) {
-    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, 3, 64, 2>(a, q, k, v, sel, o, stream);
+    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, false>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 1, 4, 64, 2, true>(a, q, k, v, sel, o, stream);
   }
-  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2>(a, q, k, v, sel, o, stream);
-  return launch<64, 8, 1, 3, 64, 2>(a, q, k, v, sel, o, stream);
+  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, false>(a, q, k, v, sel, o, stream);
+  return launch<64, 8, 1, 4, 64, 2, true>(a, q, k, v, sel, o, stream);
 }

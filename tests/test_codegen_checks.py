@@ -1,10 +1,11 @@
 """Checks on the gfx950 code the compiler generates for the kernels (CPU only:
-hipcc cross-compiles). They guard against two silent failure modes:
+hipcc cross-compiles). They guard against silent failure modes:
 
-* an inline-asm block of transposed LDS reads whose address register is
-  also one of its outputs (a read returning early would corrupt the address
-  of the reads after it);
-* register spills to scratch memory in the kernels.
+* register spills to scratch memory in the kernels (a reload's vmcnt wait
+  would also wait for every global-to-LDS copy in flight);
+* row sums that read one packed P register several times (a bit_cast of a
+  vector element reads element 0);
+* global-to-LDS copies written as inline asm without their M0 set.
 """
 import os
 import re
@@ -29,21 +30,44 @@ def _device_asm(src, tmp_path):
     return out.read_text()
 
 
-def test_transposed_read_blocks_keep_their_address(tmp_path):
-    asm = _device_asm("attend.hip", tmp_path)
-    blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", asm, re.S)
-    checked = 0
-    for blk in blocks:
-        reads = re.findall(r"ds_read_b64_tr_b16 v\[(\d+):(\d+)\], v(\d+)", blk)
-        if not reads:
+def _blocks(asm):
+    """Basic blocks as lists of instruction lines."""
+    out, cur = [], []
+    for line in asm.split("\n"):
+        if re.match(r"^(\.LBB\w+|; %bb\.\d+):", line) or line.startswith(".Lfunc_end"):
+            out.append(cur)
+            cur = []
             continue
-        addrs = {int(a) for _, _, a in reads}
-        assert len(addrs) == 1
-        addr = addrs.pop()
-        for lo, hi, _ in reads:
-            assert not (int(lo) <= addr <= int(hi)), f"output v[{lo}:{hi}] overlaps address v{addr}"
-        assert "s_waitcnt lgkmcnt(0)" in blk
-        checked += 1
+        t = line.strip()
+        if t and not t.startswith(";") and not t.startswith("."):
+            cur.append(t)
+    out.append(cur)
+    return out
+
+
+def test_row_sums_read_distinct_p_registers(tmp_path):
+    asm = _device_asm("attend.hip", tmp_path)
+    checked = 0
+    for blk in _blocks(asm):
+        srcs = [re.search(r"v_dot2c_f32_bf16_e32 v\d+, \S+, (v\d+)", i).group(1) for i in blk
+                if i.startswith("v_dot2c_f32_bf16")]
+        if len(srcs) >= 4:
+            assert len(set(srcs)) == len(srcs), srcs
+            checked += 1
+    assert checked > 0
+
+
+def test_lds_copies_set_m0(tmp_path):
+    asm = _device_asm("attend.hip", tmp_path)
+    checked = 0
+    for blk in _blocks(asm):
+        m0_set = False
+        for i in blk:
+            if re.match(r"s_\w+ m0,", i):
+                m0_set = True
+            if i.startswith("global_load_lds_dwordx4"):
+                assert m0_set, "global_load_lds without M0 set in its block"
+                checked += 1
     assert checked > 0
 
 
