@@ -87,6 +87,10 @@ __device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
   return (int32_t)(((uint64_t)(uint32_t)x * m) >> 32);
 }
 
+// A zero value row: the tail slots of a key tile load their V rows from it
+// (in the pipelined kernel), so their P.V terms vanish without masking.
+__device__ __align__(256) __bf16 vsa_zero_row[128];
+
 // Valid region of a kept or query block.
 struct Blk {
   int32_t base;     // first token row (the row of index 0)
@@ -301,10 +305,18 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const int p = s * 64 + ln;
       const int key = p / CPR, cp = p % CPR;
       const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-      const int row = key < nleft ? compact_row(kd, t * KT + key) : kd.base;
+      const bool valid = key < nleft;
+      const int row = valid ? compact_row(kd, t * KT + key) : kd.base;
       const uint32_t ro = (uint32_t)row * (uint32_t)a.sn * 2u;
+      const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
       dma16(kh, ro + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
-      dma16(vh, ro + (uint32_t)((cp ^ fv) * 16), lds_addr(vdst + s * 1024));
+      if (!PIPE || nleft >= KT) {
+        dma16(vh, ro + vo, lds_addr(vdst + s * 1024));
+      } else {
+        const unsigned char* vsrc = valid ? reinterpret_cast<const unsigned char*>(vh) + ro + vo
+                                          : reinterpret_cast<const unsigned char*>(vsa_zero_row) + vo;
+        dma16(vsrc, lds_addr(vdst + s * 1024));
+      }
     }
     const uint64_t m = nleft >= KT ? FULLM : __ballot(lane < nleft);
     ++ikt;
@@ -455,13 +467,15 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // ahead and, in the last slots, the first head-dim block's V reads; then
   // the P.V MFMAs of tile `vs_` (P of the previous step in pb) with the next
   // block's V reads and, between them, the softmax of the new scores in
-  // small pieces (masking of a tail tile, row max, exponent offset, then
-  // pairs of exponentials packed to bf16). WITH_PV false (the first tile)
-  // keeps the slots without their P.V work.
-  auto step = [&](auto with_pv, auto masked, int ks, int vs_, const bf16x8 (&pb)[QB][NKB][2], uint64_t cmask,
-                  bf16x8 (&pn)[QB][NKB][2], float (&alpha)[QB]) {
+  // small pieces (row max, exponent offset, then pairs of exponentials
+  // packed to bf16). WITH_PV false (the first tile) keeps the slots without
+  // their P.V work. Tail tiles need no masking here: their key slots past
+  // the block's end repeat the block's first row, whose score the running
+  // max has already seen (or sees in this tile), and their V rows are zero;
+  // `tail_sum` then removes those slots from the row sum.
+  auto step = [&](auto with_pv, int ks, int vs_, const bf16x8 (&pb)[QB][NKB][2], bf16x8 (&pn)[QB][NKB][2],
+                  float (&alpha)[QB]) {
     constexpr bool WITH_PV = decltype(with_pv)::value;
-    constexpr bool MASKED = decltype(masked)::value;
     static_assert(QB == 1, "the fixed schedule is written for one query block per wave");
     constexpr int KA = 4;                   // K reads ahead of their MFMA
     constexpr int NQ = NKB * NC;            // QK MFMAs
@@ -477,13 +491,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     u32x2 vr[NDB][NVR];
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mx = 0.f, mc = 0.f, psum = 0.f;
-    // slot r of 32-key block kb holds key 32kb + 8(r/4) + 4g + r%4
-    auto mask_block = [&](int kb) {
-      const uint32_t mk = (uint32_t)((cmask >> (4 * g)) >> (32 * kb));
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sa[kb][r] = ((mk >> (8 * (r >> 2) + (r & 3))) & 1u) ? sa[kb][r] : -INFINITY;
-    };
 #pragma unroll
     for (int i = 0; i < KA; ++i) kop[i] = kread(ks, i / NC, i % NC);
 #pragma unroll
@@ -514,18 +521,15 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       }
       // softmax pieces
       if (p == P_M0) {
-        if constexpr (MASKED) mask_block(0);
         mx = sa[0][0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[0][r]);
       }
       if (p == P_M1) {
 #pragma unroll
-        for (int k2 = 1; k2 < NKB; ++k2) {
-          if constexpr (MASKED) mask_block(k2);
+        for (int k2 = 1; k2 < NKB; ++k2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[k2][r]);
-        }
       }
       if (p == P_M2) {
         const f32x2 hv = halves(mx);
@@ -550,6 +554,19 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       __builtin_amdgcn_sched_barrier(0);
     }
     lrow[0] = fmaf(lrow[0], alpha[0], psum);
+  };
+
+  // Row-sum correction of a tail tile after `step`: a lane's slots past the
+  // block's end all hold the score of the block's first row, so they added
+  // the same bf16 P, which the lane's last slot (key 32(NKB-1) + 28 + 4g + 3,
+  // always among them when the lane has any) carries in the high half of
+  // its last packed word.
+  auto tail_sum = [&](uint64_t cmask, const bf16x8 (&pn)[QB][NKB][2]) {
+    const uint64_t mine = g ? 0xF0F0F0F0F0F0F0F0ull : 0x0F0F0F0F0F0F0F0Full;
+    const int ninv = __builtin_popcountll(~cmask & FULLM & mine);
+    const uint32_t last = __builtin_bit_cast(u32x4, pn[0][NKB - 1][1])[3];
+    const float pbase = __uint_as_float(last & 0xFFFF0000u);
+    lrow[0] = fmaf(-(float)ninv, pbase, lrow[0]);
   };
 
   // Publish: every wave has waited for its own loads of the tiles needed
@@ -607,76 +624,87 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     }
   };
 
-  if constexpr (PIPE) {
-    // Software pipeline. Tile t sits in stage t % NSTAGE. Step j runs QK of
-    // tile j and the P.V of tile j-1 (whose P the previous step made), with
-    // the softmax of tile j on the vector ALUs while the P.V matrix ops run.
-    // Barrier j publishes tile j; every wave has then finished step j-1, so
-    // tile j-2's stage is free and takes tile j + NSTAGE - 2.
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    bf16x8 pb[QB][NKB][2];
-    // first tile: QK and softmax only (every kept list has a tile)
-    wait_first();
-    barrier();
-    refill(AHEAD);
-    if (wave_active) {
-      float alpha[QB];
-      if (mring[0] == FULLM) step(F_{}, F_{}, 0, 0, pb, mring[0], pb, alpha);
-      else step(F_{}, T_{}, 0, 0, pb, mring[0], pb, alpha);
-      rescale(alpha);
-    }
-    shift();
-    int cur = 1, prev = 0;
-    // steady state; the step after the last tile runs the last P.V only
-#pragma unroll 1
-    while (true) {
-      const bool have = ering[0];
-      if (have) wait_first();
-      barrier();
-      refill(cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD);
-      if (!have) {
-        if (wave_active) pv(prev, pb);
-        break;
-      }
-      if (wave_active) {
-        const uint64_t cm = mring[0];
-        bf16x8 pn[QB][NKB][2];
-        float alpha[QB];
-        if (cm == FULLM) step(T_{}, F_{}, cur, prev, pb, cm, pn, alpha);
-        else step(T_{}, T_{}, cur, prev, pb, cm, pn, alpha);
-        rescale(alpha);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          pb[0][kb][0] = pn[0][kb][0];
-          pb[0][kb][1] = pn[0][kb][1];
-        }
-      }
-      prev = cur;
-      cur = cur + 1 == NSTAGE ? 0 : cur + 1;
-      shift();
-    }
-  } else {
-    int cur = 0;
-#pragma unroll 1
-    while (ering[0]) {
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // The tile loop, once for waves with query rows (ACTIVE) and once for
+  // waves without (they only load their share of the tiles and keep the
+  // barriers); two loops instead of a branch inside one keep the O
+  // accumulators in fixed registers.
+  auto run = [&](auto active) {
+    constexpr bool ACTIVE = decltype(active)::value;
+    if constexpr (PIPE) {
+      // Software pipeline. Tile t sits in stage t % NSTAGE. Step j runs QK
+      // of tile j and the P.V of tile j-1 (whose P the previous step made),
+      // with the softmax of tile j on the vector ALUs while the P.V matrix
+      // ops run. Barrier j publishes tile j; every wave has then finished
+      // step j-1, so tile j-2's stage is free and takes tile j + NSTAGE - 2.
+      bf16x8 pb[QB][NKB][2];
+      // first tile: QK and softmax only (every kept list has a tile)
       wait_first();
       barrier();
-      // refill the stage freed by the previous tile
-      refill(cur == 0 ? NSTAGE - 1 : cur - 1);
-      if (wave_active) {
-        f32x16 sa[QB][NKB];
-        bf16x8 pb[QB][NKB][2];
+      refill(AHEAD);
+      if constexpr (ACTIVE) {
         float alpha[QB];
-        qk(cur, sa);
-        softmax(sa, mring[0], mring[0] != FULLM, pb, alpha);
+        step(F_{}, 0, 0, pb, pb, alpha);
+        if (mring[0] != FULLM) tail_sum(mring[0], pb);
         rescale(alpha);
-        pv(cur, pb);
       }
       shift();
-      cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+      int cur = 1, prev = 0;
+      // steady state; the step after the last tile runs the last P.V only
+#pragma unroll 1
+      while (true) {
+        const bool have = ering[0];
+        if (have) wait_first();
+        barrier();
+        refill(cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD);
+        if (!have) {
+          if constexpr (ACTIVE) pv(prev, pb);
+          break;
+        }
+        if constexpr (ACTIVE) {
+          bf16x8 pn[QB][NKB][2];
+          float alpha[QB];
+          step(T_{}, cur, prev, pb, pn, alpha);
+          if (mring[0] != FULLM) tail_sum(mring[0], pn);
+          rescale(alpha);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            pb[0][kb][0] = pn[0][kb][0];
+            pb[0][kb][1] = pn[0][kb][1];
+          }
+        }
+        prev = cur;
+        cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+        shift();
+      }
+    } else {
+      int cur = 0;
+#pragma unroll 1
+      while (ering[0]) {
+        wait_first();
+        barrier();
+        // refill the stage freed by the previous tile
+        refill(cur == 0 ? NSTAGE - 1 : cur - 1);
+        if constexpr (ACTIVE) {
+          f32x16 sa[QB][NKB];
+          bf16x8 pb[QB][NKB][2];
+          float alpha[QB];
+          qk(cur, sa);
+          softmax(sa, mring[0], mring[0] != FULLM, pb, alpha);
+          rescale(alpha);
+          pv(cur, pb);
+        }
+        shift();
+        cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+      }
     }
+  };
+  if (!wave_active) {
+    run(F_{});
+    return;
   }
+  run(T_{});
 
   // ---- normalise and store in raster order
 #pragma unroll
