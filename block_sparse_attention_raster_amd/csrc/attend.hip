@@ -187,6 +187,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   unsigned char* kst = smem;                              // [NSTAGE][TILE_BYTES]
   unsigned char* vst = smem + NSTAGE * TILE_BYTES;        // [NSTAGE][TILE_BYTES]
   int32_t* srel = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);  // [V]
+  int32_t* ssel = srel + a.V;   // [topk] kept cubes, when topk <= VSA_ATTEND_SEL_LDS
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
   // id is remapped to give each XCD a contiguous range of (head, block) work.
@@ -215,6 +216,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       srel[s] = (tt * a.H + hh) * a.W + ww;
     }
   }
+  const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
+  const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS;
+  if (sel_lds) {
+    for (int i = tid; i < a.topk; i += NW * 64) {
+      const int c = selrow[i];
+      ssel[i] = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
+    }
+  }
   __syncthreads();
 
   const int64_t in_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
@@ -222,7 +231,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const __bf16* kh = k + in_off;
   const __bf16* vh = v + in_off;
   __bf16* oh = o + (int64_t)b * a.osb + (int64_t)h * a.osh;
-  const int32_t* selrow = sel + ((int64_t)bh * a.nq + qblk) * a.topk;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -277,12 +285,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int nkept = a.Pb + a.topk;
   auto kept_block = [&](int i) -> int {
     if (i < a.Pb) return i;
+    if (sel_lds) return a.Pb + __builtin_amdgcn_readfirstlane(ssel[i - a.Pb]);
     int c = selrow[i - a.Pb];
     c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
     return a.Pb + c;
   };
   int ibi = 0, ikt = 0;
   Blk kd = describe_block(a, kept_block(0), KT);
+  const uint32_t last_row = (uint32_t)(a.P + a.T * a.H * a.W - 1);  // bound of every load row
 
   // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
   // for s = wave*SPW + j: key row (s*64 + lane)/CPR, chunk position
@@ -307,7 +317,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
       const bool valid = key < nleft;
       const int row = valid ? compact_row(kd, t * KT + key) : kd.base;
-      const uint32_t ro = (uint32_t)row * (uint32_t)a.sn * 2u;
+      const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.sn * 2u;
       const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
       dma16(kh, ro + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
       if (!PIPE || nleft >= KT) {
@@ -326,6 +336,98 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       if (ibi < nkept) kd = describe_block(a, kept_block(ibi), KT);
     }
     return m;
+  };
+
+  // Pipelined kernel: the walker describes the next tile in scalar
+  // registers outside the compute step (branches, block descriptors), and
+  // the step itself forms the per-lane load addresses (branch-free vector
+  // work in its QK half, where the vector ALU is otherwise idle) and issues
+  // the copies, spread over its MFMA slots. Whole cubes with KT a multiple of
+  // ch*cw use this thread's row offsets within a tile, read from the slot
+  // table once here; other blocks unravel the compact index with
+  // multiply-high divisions (whole cubes too: their extents are the cube's).
+  struct Spec {
+    int32_t base;    // first token row of the block
+    int32_t nleft;   // valid slots from this tile on (KT or more: all)
+    int32_t k0;      // compact index of the tile's first slot
+    int32_t trow;    // whole cubes: row offset of the tile
+    int32_t mode;    // 0 whole cube, 1 prefix, 2 unravel, 3 nothing left
+    int32_t ew, ehw;
+    uint64_t mw, mhw;
+  };
+  struct Pend {
+    uint32_t ko[SPW];              // K byte offsets from kh
+    const unsigned char* va[SPW];  // V source addresses (zero row for tail slots)
+  };
+  const int chw = a.ch * a.cw;
+  const bool fastshape = (KT % chw) == 0;
+  const int64_t tile_rows = (int64_t)(KT / chw) * a.H * a.W;
+  int srk[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int key = ((wave * SPW + j) * 64 + lane) / CPR;
+    srk[j] = (PIPE && fastshape && key < a.V) ? srel[key] : 0;
+  }
+  // describes the walker's current tile as ring slot AHEAD, then advances
+  auto spec = [&](Spec& sp, uint64_t& m, bool& e) {
+    const bool any = ibi < nkept;
+    const int t = ikt;
+    sp.base = any ? kd.base : 0;
+    sp.nleft = any ? kd.n - t * KT : KT;
+    sp.k0 = t * KT;
+    sp.trow = (int32_t)(t * tile_rows);
+    sp.mode = !any ? 3 : kd.prefix ? 1 : (kd.full && fastshape) ? 0 : 2;
+    sp.ew = kd.ew;
+    sp.ehw = kd.ehw;
+    sp.mw = kd.mw;
+    sp.mhw = kd.mhw;
+    e = any;
+    m = sp.nleft >= KT ? FULLM : ((1ull << sp.nleft) - 1ull);
+    if (any) {
+      ++ikt;
+      if (ikt >= kd.ntiles) {
+        ikt = 0;
+        ++ibi;
+        if (ibi < nkept) kd = describe_block(a, kept_block(ibi), KT);
+      }
+    }
+  };
+  // per-lane addresses of this thread's load j of the tile `sp` describes
+  auto addrs = [&](const Spec& sp, Pend& pd, int j) {
+    const int p = (wave * SPW + j) * 64 + lane;
+    const int key = p / CPR, cp = p % CPR;
+    const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+    const bool valid = key < sp.nleft;
+    const int kc = sp.k0 + key;
+    const int tt = fast_div(kc, sp.mhw);
+    const int r = kc - tt * sp.ehw;
+    const int hh = fast_div(r, sp.mw);
+    const int ww = r - hh * sp.ew;
+    // blend the three row formulas with opaque uniform masks: a select on a
+    // uniform condition would become a branch and split the fenced step
+    // (and the per-lane validity likewise: a divergent branch)
+    // Past the walker's last tile (mode 3) the extents are stale: row 0.
+    int m_pre = -(int)(sp.mode == 1), m_whole = -(int)(sp.mode == 0), m_val = -(int)valid;
+    int m_none = -(int)(sp.mode == 3);
+    asm volatile("" : "+v"(m_pre), "+v"(m_whole), "+v"(m_val), "+v"(m_none));
+    int row = sp.base + (tt * a.H + hh) * a.W + ww;
+    row = (row & ~m_pre) | ((sp.base + kc) & m_pre);
+    row = (row & ~m_whole) | ((sp.base + sp.trow + srk[j]) & m_whole);
+    row = (row & m_val) | (sp.base & ~m_val);
+    row &= ~m_none;
+    // guard: never address past the last token row
+    const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.sn * 2u;
+    const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
+    pd.ko[j] = ro + (uint32_t)((cp ^ (key & KSWZ)) * 16);
+    const uint64_t vv = (uint64_t)reinterpret_cast<uintptr_t>(vh) + ro + vo;
+    const uint64_t vz = (uint64_t)reinterpret_cast<uintptr_t>(vsa_zero_row) + vo;
+    const uint64_t mv64 = (uint64_t)(int64_t)m_val;
+    pd.va[j] = reinterpret_cast<const unsigned char*>((vv & mv64) | (vz & ~mv64));
+  };
+  auto fire = [&](const Pend& pd, int stage, int j) {
+    const int s = wave * SPW + j;
+    dma16(kh, pd.ko[j], lds_addr(kst + stage * TILE_BYTES + s * 1024));
+    dma16(pd.va[j], lds_addr(vst + stage * TILE_BYTES + s * 1024));
   };
 
   // per-lane LDS offsets of the MFMA operands
@@ -474,10 +576,10 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // max has already seen (or sees in this tile), and their V rows are zero;
   // `tail_sum` then removes those slots from the row sum.
   auto step = [&](auto with_pv, int ks, int vs_, const bf16x8 (&pb)[QB][NKB][2], bf16x8 (&pn)[QB][NKB][2],
-                  float (&alpha)[QB]) {
+                  float (&alpha)[QB], const Spec& sp, int fstage) {
     constexpr bool WITH_PV = decltype(with_pv)::value;
     static_assert(QB == 1, "the fixed schedule is written for one query block per wave");
-    constexpr int KA = 4;                   // K reads ahead of their MFMA
+    constexpr int KA = 6;                   // K reads ahead of their MFMA
     constexpr int NQ = NKB * NC;            // QK MFMAs
     constexpr int NDB = D / 32;             // head-dim blocks of P.V
     constexpr int PPD = 2 * NKB;            // P.V MFMAs per head-dim block
@@ -489,6 +591,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     f32x16 sa[NKB];
     bf16x8 kop[NQ];
     u32x2 vr[NDB][NVR];
+    Pend pd;
+    static_assert(1 + 2 * (SPW - 1) < NQ / 2, "addresses before their copies");
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mx = 0.f, mc = 0.f, psum = 0.f;
 #pragma unroll
@@ -504,6 +608,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       }
       const int kb = q / NC, c = q % NC;
       sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[q], qreg[0][c], c == 0 ? f32x16{} : sa[kb], 0, 0, 0);
+      // the refill of the stage freed by this step's barrier: addresses of
+      // load j in slot 1 + 2j, its copies in slot NQ/2 + 2j
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        if (q == 1 + 2 * j) addrs(sp, pd, j);
+        if (q == NQ / 2 + 2 * j) fire(pd, fstage, j);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -637,17 +748,29 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       // of tile j and the P.V of tile j-1 (whose P the previous step made),
       // with the softmax of tile j on the vector ALUs while the P.V matrix
       // ops run. Barrier j publishes tile j; every wave has then finished
-      // step j-1, so tile j-2's stage is free and takes tile j + NSTAGE - 2.
+      // step j-1, so tile j-2's stage is free, and step j issues the copies
+      // of tile j + NSTAGE - 2 into it (prepared before the barrier).
       bf16x8 pb[QB][NKB][2];
+      Spec sp;
+      auto fire_all = [&](int stage) {
+        Pend pd;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          addrs(sp, pd, j);
+          fire(pd, stage, j);
+        }
+      };
       // first tile: QK and softmax only (every kept list has a tile)
+      spec(sp, mring[AHEAD], ering[AHEAD]);
       wait_first();
       barrier();
-      refill(AHEAD);
       if constexpr (ACTIVE) {
         float alpha[QB];
-        step(F_{}, 0, 0, pb, pb, alpha);
+        step(F_{}, 0, 0, pb, pb, alpha, sp, AHEAD);
         if (mring[0] != FULLM) tail_sum(mring[0], pb);
         rescale(alpha);
+      } else {
+        fire_all(AHEAD);
       }
       shift();
       int cur = 1, prev = 0;
@@ -655,9 +778,10 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 #pragma unroll 1
       while (true) {
         const bool have = ering[0];
+        const int fst = cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD;
+        if (have) spec(sp, mring[AHEAD], ering[AHEAD]);
         if (have) wait_first();
         barrier();
-        refill(cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD);
         if (!have) {
           if constexpr (ACTIVE) pv(prev, pb);
           break;
@@ -665,7 +789,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         if constexpr (ACTIVE) {
           bf16x8 pn[QB][NKB][2];
           float alpha[QB];
-          step(T_{}, cur, prev, pb, pn, alpha);
+          step(T_{}, cur, prev, pb, pn, alpha, sp, fst);
           if (mring[0] != FULLM) tail_sum(mring[0], pn);
           rescale(alpha);
 #pragma unroll
@@ -673,6 +797,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
             pb[0][kb][0] = pn[0][kb][0];
             pb[0][kb][1] = pn[0][kb][1];
           }
+        } else {
+          fire_all(fst);
         }
         prev = cur;
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
@@ -729,7 +855,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
-  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.V * 4;
+  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.V * 4 +
+                    (a.topk <= VSA_ATTEND_SEL_LDS ? (size_t)a.topk * 4 : 0);
   if (lds > 65536) {
     static bool raised = false;  // benign race: the attribute call is idempotent
     if (!raised) {
