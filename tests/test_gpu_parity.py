@@ -73,6 +73,10 @@ SMALL = [
     ("topk_one", 1, 2, 128, (8, 12, 16), (4, 4, 4), 1, 0),
     ("tiny_cubes", 1, 2, 128, (3, 4, 5), (1, 2, 2), 7, 3),
     ("odd_cube_v60", 1, 2, 64, (7, 9, 10), (3, 4, 5), 4, 0),
+    # tail extents eh = 1, ew = 2: division magics of 2 (2^31) and 1 (2^32)
+    ("tail_extents_1_2", 1, 2, 128, (5, 9, 18), (4, 8, 8), 4, 0),
+    # tail tiles with more than 32 valid slots (a mask word of all ones)
+    ("tail_tile_40", 1, 2, 128, (5, 13, 16), (4, 8, 8), 3, 40),
 ]
 
 
