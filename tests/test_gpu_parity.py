@@ -109,6 +109,36 @@ def test_all_blocks_equals_dense_attention():
         assert e["max_abs"] <= G.MAX_ABS and e["rel_l2"] <= G.REL_L2, e
 
 
+def test_scores_far_above_the_first_tiles_offset():
+    """Every row's first tiles (the prefix, keys near zero) score about 0;
+    the selected video cubes (keys near 2, queries near 1) score about 256,
+    i.e. p = 2^32.6 against the first tiles' exponent offset. Those tiles take
+    the recompute path of the pipelined kernel (whole and tail tiles alike);
+    the result must still match the oracle."""
+    w = synthetic.custom_workload("offset_overflow", seed=21, batch=1, heads=2, head_dim=128,
+                                  latent=(9, 10, 11), cube=(4, 8, 8), topk=3, prefix_len=100)
+    rng = np.random.default_rng(21)
+    N = w.prefix_len + int(np.prod(w.latent))
+    g = O.geometry(w.latent, w.cube, w.prefix_len)
+    q = 1.0 + 0.05 * rng.standard_normal((1, 2, N, 128))
+    k = 0.1 * rng.standard_normal((1, 2, N, 128))
+    # hot: cubes 0 (whole), 5 (96 tokens) and 11 (6 tokens), and prefix tokens
+    # 64..99, the prefix block's tail tile, which is each row's second tile
+    hot = np.isin(g.block_of_token - g.num_prefix_blocks, [0, 5, 11])
+    hot[64:100] = True
+    k[:, :, hot, :] += 2.0
+    v = rng.standard_normal((1, 2, N, 128))
+    bits = tuple(synthetic.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    _announce("exponent-offset overflow recompute")
+    res = G.run_gpu(w, 3, bits)
+    g2, qbar, kbar, scores = G.oracle_scores(w, bits[0], bits[1])
+    chk = O.check_selection(res["sel"], scores, 3, band=G.TIE_BAND)
+    assert chk["mismatch_rows"] == [], chk["mismatch_rows"][:10]
+    assert set(np.unique(res["sel"]).tolist()) == {0, 5, 11}
+    worst = G.check_outputs(w, g2, res, [(0, 0), (0, 1)])
+    assert worst["max_abs"] <= G.MAX_ABS and worst["rel_l2"] <= G.REL_L2, worst
+
+
 def test_constant_values_give_constant_output():
     """V == 1 everywhere: each softmax row sums to one, so O == 1 exactly in
     bf16 up to the rounding of the normaliser."""
