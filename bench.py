@@ -2,7 +2,7 @@
 every (batch, head)) of the block-sparse path on synthetic inputs resident in
 HBM. Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload wan]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload wan] [--dtype bf16]
 
 Throughput is selected-block TFLOP/s: 4 * head_dim * sum over query tokens of
 the number of key tokens in their kept blocks (QK^T and PV; the selection of
@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "ms per attention call + selected-block TFLOP/s (% bf16 MFMA peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_MFMA_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": 2500.0}   # fp16 dense peak equals bf16's
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend.json")
 ATTEND_SOURCES = ["attend.hip", "vsa_device.h", "vsa_limits.h"]
@@ -63,7 +64,7 @@ def traffic_for(workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, bits, sel_np, flops_total, budget_s: float = 12.0):
+def cpu_baseline(w, bits, sel_np, flops_total, budget_s: float = 12.0, dtype: str = "bf16"):
     """Time the CPU oracle (float64, dense-masked) on whole (batch, head)
     pairs: pool + score + top-k of the head and attention of all its query
     blocks, head after head until about ``budget_s`` seconds have been spent
@@ -82,7 +83,7 @@ def cpu_baseline(w, bits, sel_np, flops_total, budget_s: float = 12.0):
     for bh in range(BH):
         b, h = divmod(bh, w.heads)
         t0 = time.perf_counter()
-        qf, kf, vf = (O.decode_bf16(x[b, h]) for x in (q_b, k_b, v_b))
+        qf, kf, vf = (O.decode(x[b, h], dtype) for x in (q_b, k_b, v_b))
         s = O.block_scores(O.pool(qf, g), O.pool(kf, g, video_only=True), w.head_dim)
         sel0 = O.select_topk(s, w.topk)
         t_sel = time.perf_counter() - t0
@@ -128,6 +129,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--topk", type=int, default=None)
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
+                    help="element type of q, k, v and the output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (the "
@@ -160,8 +163,8 @@ def main(argv=None):
                                (topk,), w.prefix_len, w.modification)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    bits = synthetic.make_inputs(w)
-    q, k, v = (synthetic.bits_to_torch(x, dev) for x in bits)
+    bits = synthetic.make_inputs(w, dtype=args.dtype)
+    q, k, v = (synthetic.bits_to_torch(x, dev, args.dtype) for x in bits)
     pl = vsa.plan_for(q, w.latent, w.cube, topk, w.prefix_len)
     ws = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
     sel = torch.empty((pl.batch, pl.heads, pl.num_q_blocks, topk), dtype=torch.int32, device=dev)
@@ -195,7 +198,8 @@ def main(argv=None):
     flops = selected_flops(pl, sel_np)
     value = flops / (ms_per_step * 1e-3) / 1e12
     att_tflops = flops / (att_ms * 1e-3) / 1e12
-    traffic = traffic_for(w.name)
+    traffic = traffic_for(w.name if args.dtype == "bf16" else f"{w.name}_{args.dtype}")
+    peak = PEAK_MFMA_TFLOPS[args.dtype]
     line = {
         "metric": METRIC,
         "value": value,
@@ -207,7 +211,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
@@ -222,14 +226,14 @@ def main(argv=None):
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attend_pct_bf16_peak": 100.0 * att_tflops / PEAK_BF16_TFLOPS,
         "roofline": {
-            "bound": "mfma", "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": att_tflops / PEAK_BF16_TFLOPS,
+            "bound": "mfma", "achieved": att_tflops, "peak": peak, "unit": "TFLOP/s",
+            "frac": att_tflops / peak,
             "traffic": traffic,
             "kernel": "vsa_attend_kernel",
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, bits, sel_np, flops)
+        line["cpu_baseline"] = cpu_baseline(w, bits, sel_np, flops, dtype=args.dtype)
     print(json.dumps(line), flush=True)
     return 0
 

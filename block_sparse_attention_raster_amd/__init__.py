@@ -9,8 +9,9 @@ load the library; the first call does, and raises if it is missing.
     import block_sparse_attention_raster_amd as vsa
     out = vsa.forward(q, k, v, latent_shape=(31, 22, 40), cube_shape=(4, 8, 8), topk=64)
 
-q, k, v: bfloat16 CUDA (HIP) tensors [B, heads, N, head_dim] with the last
-dimension contiguous and N = prefix_len + T*H*W tokens in raster order.
+q, k, v: bfloat16 or float16 CUDA (HIP) tensors [B, heads, N, head_dim] of
+one dtype, with the last dimension contiguous and N = prefix_len + T*H*W
+tokens in raster order. The output has their dtype.
 """
 from __future__ import annotations
 
@@ -55,13 +56,19 @@ class Plan:
         return f"Plan({describe(self)})"
 
 
+_DTYPES = {"bf16": _lib.VSA_DTYPE_BF16, "f16": _lib.VSA_DTYPE_F16}
+
+
 def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Sequence[int], topk: int,
          prefix_len: int = 0, strides: Optional[Sequence[int]] = None,
-         o_strides: Optional[Sequence[int]] = None) -> Plan:
+         o_strides: Optional[Sequence[int]] = None, dtype: str = "bf16") -> Plan:
     """Validate a problem and derive its geometry (vsa_plan). ``strides``
     are the (b, h, n) element strides shared by q, k and v; the default is
     a contiguous [B, heads, N, head_dim] layout. ``o_strides`` default to
-    ``strides``."""
+    ``strides``. ``dtype`` is "bf16" or "f16", the element type of q, k, v
+    and o."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(_DTYPES)}, got {dtype!r}")
     N = int(prefix_len) + int(latent[0]) * int(latent[1]) * int(latent[2])
     if strides is None:
         strides = (heads * N * head_dim, N * head_dim, head_dim)
@@ -71,7 +78,7 @@ def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Seq
     pr.batch, pr.heads, pr.head_dim = int(batch), int(heads), int(head_dim)
     pr.latent[:] = [int(x) for x in latent]
     pr.cube[:] = [int(x) for x in cube]
-    pr.topk, pr.prefix_len, pr.dtype = int(topk), int(prefix_len), _lib.VSA_DTYPE_BF16
+    pr.topk, pr.prefix_len, pr.dtype = int(topk), int(prefix_len), _DTYPES[dtype]
     pr.stride_b, pr.stride_h, pr.stride_n = (int(s) for s in strides)
     pr.o_stride_b, pr.o_stride_h, pr.o_stride_n = (int(s) for s in o_strides)
     raw = _lib.VsaPlan()
@@ -79,12 +86,17 @@ def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Seq
     return Plan(raw)
 
 
-def _check_qkv(t, name, shape, strides):
+def _torch_dtype(pl: Plan):
+    import torch
+    return torch.float16 if pl.dtype == _lib.VSA_DTYPE_F16 else torch.bfloat16
+
+
+def _check_qkv(t, name, shape, strides, dtype):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (the plan's dtype), got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
     if tuple(t.shape) != tuple(shape):
@@ -96,10 +108,14 @@ def _check_qkv(t, name, shape, strides):
 
 def plan_for(q, latent: Sequence[int], cube: Sequence[int], topk: int, prefix_len: int = 0,
              out=None) -> Plan:
-    """Plan from q's shape and strides (and out's strides, if given)."""
+    """Plan from q's shape, strides and dtype (and out's strides, if given)."""
+    import torch
     B, Hh, N, D = q.shape
     o_strides = out.stride()[:3] if out is not None else q.stride()[:3]
-    return plan(B, Hh, D, latent, cube, topk, prefix_len, q.stride()[:3], o_strides)
+    names = {torch.bfloat16: "bf16", torch.float16: "f16"}
+    if q.dtype not in names:
+        raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
+    return plan(B, Hh, D, latent, cube, topk, prefix_len, q.stride()[:3], o_strides, names[q.dtype])
 
 
 def _stream_ptr(device):
@@ -114,8 +130,9 @@ def select(pl: Plan, q, k, workspace=None, sel=None):
     import torch
     shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
     strides = (pl.stride_b, pl.stride_h, pl.stride_n)
-    _check_qkv(q, "q", shape, strides)
-    _check_qkv(k, "k", shape, strides)
+    dt = _torch_dtype(pl)
+    _check_qkv(q, "q", shape, strides, dt)
+    _check_qkv(k, "k", shape, strides, dt)
     dev = q.device
     if workspace is None:
         workspace = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
@@ -137,14 +154,15 @@ def attend(pl: Plan, q, k, v, sel, out=None):
     import torch
     shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
     strides = (pl.stride_b, pl.stride_h, pl.stride_n)
+    dt = _torch_dtype(pl)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_qkv(t, n, shape, strides)
+        _check_qkv(t, n, shape, strides, dt)
     dev = q.device
     if out is None:
         out = torch.empty_strided(shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n, 1),
-                                  dtype=torch.bfloat16, device=dev)
+                                  dtype=dt, device=dev)
     else:
-        _check_qkv(out, "out", shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n))
+        _check_qkv(out, "out", shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n), dt)
     if sel.dtype != torch.int32 or sel.numel() != pl.sel_elems or not sel.is_contiguous():
         raise ValueError("sel must be a contiguous int32 tensor of plan.sel_elems elements")
     with torch.cuda.device(dev):

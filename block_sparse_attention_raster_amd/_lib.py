@@ -16,6 +16,7 @@ VSA_ERR_OVERFLOW = -5
 VSA_ERR_DEVICE = -6
 VSA_ERR_LAUNCH = -7
 VSA_DTYPE_BF16 = 0
+VSA_DTYPE_F16 = 1
 
 EXPORTED = ("vsa_plan", "vsa_select", "vsa_attend", "vsa_forward", "vsa_describe",
             "vsa_status_str")

@@ -88,6 +88,7 @@ VsaArgs make_args(const vsa_plan_t& pl) {
   a.tiles = pl.attend_tiles;
   a.magic_nW = ((1ull << 32) + (uint64_t)a.nW - 1) / (uint64_t)a.nW;
   a.magic_nH = ((1ull << 32) + (uint64_t)a.nH - 1) / (uint64_t)a.nH;
+  a.f16 = p.dtype == VSA_DTYPE_F16;
   auto magic = [](int64_t d) { return ((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d; };
   const int64_t tail_h = a.H - (int64_t)(a.nH - 1) * a.ch, tail_w = a.W - (int64_t)(a.nW - 1) * a.cw;
   const int64_t ehs[2] = {a.ch, tail_h}, ews[2] = {a.cw, tail_w};

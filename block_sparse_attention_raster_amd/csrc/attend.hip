@@ -67,6 +67,43 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit element type of q, k, v, o and of P: bf16, or fp16 (the user
+// guide's Wan route takes either, section "Verify routing and fallback").
+// MFMA operands travel as raw 16-bit lanes (bf16x8 containers).
+template <bool F16>
+struct Elem {
+  // two floats to one packed pair (round to nearest even)
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) { return pack_bf16x2(x, y); }
+  static __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // acc + both elements of a packed pair
+  static __device__ __forceinline__ float add2(uint32_t p, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), ones, acc, false);
+  }
+  // the high element of a packed pair as a float
+  static __device__ __forceinline__ float hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+};
+template <>
+struct Elem<true> {
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+  }
+  static __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  static __device__ __forceinline__ float add2(uint32_t p, float acc) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, acc, false);
+  }
+  static __device__ __forceinline__ float hi(uint32_t p) { return (float)__builtin_bit_cast(f16x2, p)[1]; }
+};
+
 // The values of x held by lanes l % 32 and 32 + l % 32 (the two halves of a
 // query row's keys), in every lane l: one v_permlane32_swap, which exchanges
 // the upper half of its first operand with the lower half of its second.
@@ -161,16 +198,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE, bool F16>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
                                                              const __bf16* __restrict__ k,
                                                              const __bf16* __restrict__ v,
                                                              const int32_t* __restrict__ sel,
                                                              __bf16* __restrict__ o) {
+  using E = Elem<F16>;
   constexpr int CPR = D / 8;             // 16-byte chunks per key row
   constexpr int NKB = KT / 32;           // 32-key MFMA blocks per tile
-  constexpr uint64_t FULLM = KT == 64 ? ~0ull : ((1ull << KT) - 1ull);
+  constexpr uint64_t FULLM = KT == 64 ? ~0ull : ((1ull << (KT & 63)) - 1ull);
   static_assert(KT == 32 || KT == 64, "key tile of 32 or 64 slots");
   constexpr int RW = NW * 32 * QB;       // query slots per workgroup
   constexpr int UNITS = KT * CPR;        // 16-byte units per K (or V) tile
@@ -471,7 +509,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][c], qreg[qb][c], sacc[qb][kb], 0, 0, 0);
+          sacc[qb][kb] = E::mfma(kop[kb][c], qreg[qb][c], sacc[qb][kb]);
     }
   };
 
@@ -491,7 +529,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
           const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[qb][kb][hh], oacc[qb][db], 0, 0, 0);
+            oacc[qb][db] = E::mfma(vop, pb[qb][kb][hh], oacc[qb][db]);
         }
     }
   };
@@ -532,7 +570,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const float mc = mx > mold + kRescaleLog2 ? mx : mold;
       alpha[qb] = __builtin_amdgcn_exp2f(mold - mc);
       mrow[qb] = mc;
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -543,9 +580,9 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
           for (int i = 0; i < 4; ++i) {
             const int r = 8 * hh + 2 * i;
             // (a bit_cast of the vector element w[i] would read element 0)
-            const uint32_t pw = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], cexp, -mc)),
+            const uint32_t pw = E::pack2(__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], cexp, -mc)),
                                             __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r + 1], cexp, -mc)));
-            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), ones, psum, false);
+            psum = E::add2(pw, psum);
             w[i] = pw;
           }
           pb[qb][kb][hh] = __builtin_bit_cast(bf16x8, w);
@@ -593,7 +630,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     u32x2 vr[NDB][NVR];
     Pend pd;
     static_assert(1 + 2 * (SPW - 1) < NQ / 2, "addresses before their copies");
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mx = 0.f, mc = 0.f, psum = 0.f;
 #pragma unroll
     for (int i = 0; i < KA; ++i) kop[i] = kread(ks, i / NC, i % NC);
@@ -607,7 +643,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         vr[0][i + 1] = vread(vs_, 0, i + 1);
       }
       const int kb = q / NC, c = q % NC;
-      sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[q], qreg[0][c], c == 0 ? f32x16{} : sa[kb], 0, 0, 0);
+      sa[kb] = E::mfma(kop[q], qreg[0][c], c == 0 ? f32x16{} : sa[kb]);
       // the refill of the stage freed by this step's barrier: addresses of
       // load j in slot 1 + 2j, its copies in slot NQ/2 + 2j
 #pragma unroll
@@ -628,7 +664,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         const u32x4 w = {vr[db][4 * kb + 2 * hh][0], vr[db][4 * kb + 2 * hh][1], vr[db][4 * kb + 2 * hh + 1][0],
                          vr[db][4 * kb + 2 * hh + 1][1]};
         oacc[0][db] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[0][kb][hh], oacc[0][db], 0, 0, 0);
+            E::mfma(__builtin_bit_cast(bf16x8, w), pb[0][kb][hh], oacc[0][db]);
       }
       // softmax pieces
       if (p == P_M0) {
@@ -654,9 +690,9 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       for (int k = 0; k < NPAIR; ++k) {
         if (p == P_PAIR0 + (k * (NP - P_PAIR0)) / NPAIR) {
           const int pkb = k / 8, phh = (k % 8) / 4, i = k % 4, r = 8 * phh + 2 * i;
-          const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sa[pkb][r], cexp, -mc)),
+          const uint32_t w = E::pack2(__builtin_amdgcn_exp2f(fmaf(sa[pkb][r], cexp, -mc)),
                                          __builtin_amdgcn_exp2f(fmaf(sa[pkb][r + 1], cexp, -mc)));
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, psum, false);
+          psum = E::add2(w, psum);
           u32x4 t = __builtin_bit_cast(u32x4, pn[0][pkb][phh]);
           t[i] = w;
           pn[0][pkb][phh] = __builtin_bit_cast(bf16x8, t);
@@ -676,7 +712,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     const uint64_t mine = g ? 0xF0F0F0F0F0F0F0F0ull : 0x0F0F0F0F0F0F0F0Full;
     const int ninv = __builtin_popcountll(~cmask & FULLM & mine);
     const uint32_t last = __builtin_bit_cast(u32x4, pn[0][NKB - 1][1])[3];
-    const float pbase = __uint_as_float(last & 0xFFFF0000u);
+    const float pbase = E::hi(last);
     lrow[0] = fmaf(-(float)ninv, pbase, lrow[0]);
   };
 
@@ -844,15 +880,15 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           u32x2 w;
-          w[0] = pack_bf16x2(oacc[qb][db][4 * r4] * inv, oacc[qb][db][4 * r4 + 1] * inv);
-          w[1] = pack_bf16x2(oacc[qb][db][4 * r4 + 2] * inv, oacc[qb][db][4 * r4 + 3] * inv);
+          w[0] = E::pack2(oacc[qb][db][4 * r4] * inv, oacc[qb][db][4 * r4 + 1] * inv);
+          w[1] = E::pack2(oacc[qb][db][4 * r4 + 2] * inv, oacc[qb][db][4 * r4 + 3] * inv);
           *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * r4) = w;
         }
     }
   }
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE, bool F16>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
   const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.V * 4 +
@@ -861,7 +897,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
     static bool raised = false;  // benign race: the attribute call is idempotent
     if (!raised) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE>),
+          reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>),
           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
       raised = true;
@@ -869,7 +905,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   }
   const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * a.tiles;
   dim3 grid((unsigned)((nwg + 7) / 8 * 8));
-  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE>), grid, dim3(NW * 64), lds, stream, a,
+  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>), grid, dim3(NW * 64), lds, stream, a,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();
 }
@@ -879,13 +915,20 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
 // Tilings: cubes of up to 64 tokens use 2-wave workgroups (64 query rows)
 // with 32-key tiles, so four workgroups share a CU and each SIMD runs two
 // independent waves; larger cubes use 8-wave workgroups (256 query rows)
-// with 64-key tiles three stages deep.
+// with 64-key tiles four stages deep and the software-pipelined step.
+template <bool F16>
+static hipError_t dispatch(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
+                           const int32_t* sel, void* o, hipStream_t stream) {
+  if (a.D == 128) {
+    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, false, F16>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 1, 4, 64, 2, true, F16>(a, q, k, v, sel, o, stream);
+  }
+  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, false, F16>(a, q, k, v, sel, o, stream);
+  return launch<64, 8, 1, 4, 64, 2, true, F16>(a, q, k, v, sel, o, stream);
+}
+
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                              const int32_t* sel, void* o, hipStream_t stream) {
-  if (a.D == 128) {
-    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, false>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, 4, 64, 2, true>(a, q, k, v, sel, o, stream);
-  }
-  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, false>(a, q, k, v, sel, o, stream);
-  return launch<64, 8, 1, 4, 64, 2, true>(a, q, k, v, sel, o, stream);
+  return a.f16 ? dispatch<true>(a, variant, q, k, v, sel, o, stream)
+               : dispatch<false>(a, variant, q, k, v, sel, o, stream);
 }

@@ -45,7 +45,7 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   if (p.stride_b < 1 || p.stride_h < 1 || p.stride_n < 1 || p.o_stride_b < 1 ||
       p.o_stride_h < 1 || p.o_stride_n < 1)
     return VSA_ERR_INVALID_ARG;
-  if (p.dtype != VSA_DTYPE_BF16) return VSA_ERR_UNSUPPORTED;
+  if (p.dtype != VSA_DTYPE_BF16 && p.dtype != VSA_DTYPE_F16) return VSA_ERR_UNSUPPORTED;
   if (p.head_dim != 64 && p.head_dim != 128) return VSA_ERR_UNSUPPORTED;
 
   const int64_t T = p.latent[0], H = p.latent[1], W = p.latent[2];

@@ -4,7 +4,7 @@
 // q for every query block (prefix blocks and cubes), k for every cube. Only
 // the block's valid tokens are read and the sum is divided by their count.
 // Reads go through the in-kernel index map, 16 bytes per lane; the sum is
-// float32 and the result float32.
+// float32 and the result float32. Inputs are bf16 or fp16.
 
 #include "vsa_device.h"
 
@@ -12,7 +12,7 @@ namespace {
 
 constexpr int kPoolThreads = 256;
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(kPoolThreads) void vsa_pool_kernel(VsaArgs a, const __bf16* __restrict__ q,
                                                                 const __bf16* __restrict__ k,
                                                                 float* __restrict__ qbar,
@@ -45,8 +45,13 @@ __global__ __launch_bounds__(kPoolThreads) void vsa_pool_kernel(VsaArgs a, const
     const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)row * a.sn + c * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += __uint_as_float(x[i] << 16);
-      acc[2 * i + 1] += __uint_as_float(x[i] & 0xFFFF0000u);
+      if constexpr (F16) {   // fp16 inputs (exact in float)
+        acc[2 * i] += (float)__builtin_bit_cast(_Float16, (unsigned short)(x[i] & 0xFFFFu));
+        acc[2 * i + 1] += (float)__builtin_bit_cast(_Float16, (unsigned short)(x[i] >> 16));
+      } else {               // bf16: the upper half of a float
+        acc[2 * i] += __uint_as_float(x[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(x[i] & 0xFFFF0000u);
+      }
     }
   }
 #pragma unroll
@@ -62,14 +67,20 @@ __global__ __launch_bounds__(kPoolThreads) void vsa_pool_kernel(VsaArgs a, const
 
 }  // namespace
 
-hipError_t vsa_launch_pool(const VsaArgs& a, const void* q, const void* k, float* qbar, float* kbar,
-                           hipStream_t stream) {
+template <bool F16>
+static void launch_pool(const VsaArgs& a, const void* q, const void* k, float* qbar, float* kbar, hipStream_t stream) {
   dim3 grid((a.nq + a.nb) * a.B * a.Hh);
   if (a.D == 128)
-    hipLaunchKernelGGL(vsa_pool_kernel<128>, grid, dim3(kPoolThreads), 0, stream, a,
-                       (const __bf16*)q, (const __bf16*)k, qbar, kbar);
+    hipLaunchKernelGGL((vsa_pool_kernel<128, F16>), grid, dim3(kPoolThreads), 0, stream, a, (const __bf16*)q,
+                       (const __bf16*)k, qbar, kbar);
   else
-    hipLaunchKernelGGL(vsa_pool_kernel<64>, grid, dim3(kPoolThreads), 0, stream, a,
-                       (const __bf16*)q, (const __bf16*)k, qbar, kbar);
+    hipLaunchKernelGGL((vsa_pool_kernel<64, F16>), grid, dim3(kPoolThreads), 0, stream, a, (const __bf16*)q,
+                       (const __bf16*)k, qbar, kbar);
+}
+
+hipError_t vsa_launch_pool(const VsaArgs& a, const void* q, const void* k, float* qbar, float* kbar,
+                           hipStream_t stream) {
+  if (a.f16) launch_pool<true>(a, q, k, qbar, kbar, stream);
+  else launch_pool<false>(a, q, k, qbar, kbar, stream);
   return hipGetLastError();
 }

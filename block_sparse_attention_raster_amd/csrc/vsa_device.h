@@ -38,6 +38,7 @@ struct VsaArgs {
   int32_t tiles;         // query row tiles per query block
   uint64_t magic_nW;     // ceil(2^32 / nW): floor(x / nW) = (x * magic) >> 32 for x < 2^16
   uint64_t magic_nH;     // ceil(2^32 / nH)
+  int32_t f16;           // q, k, v, o are fp16 (else bf16)
   // Division magics of the valid extents of cubes: ew in {cw, W - (nW-1)*cw}
   // (index 0: whole, 1: tail) and eh*ew with index 2*[eh is the tail] +
   // [ew is the tail].

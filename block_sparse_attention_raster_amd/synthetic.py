@@ -17,8 +17,8 @@ Recipe, for every workload:
   2. draw q, k, v in that order, each rng.standard_normal((B, Hh, N, D),
      dtype=float32), layout [B, Hh, N, D] with tokens in raster order;
   3. apply the workload's modification in float32 (see ``_modify``);
-  4. round to bfloat16 with round-to-nearest-even; the result is returned
-     as the raw uint16 bit patterns.
+  4. round to bfloat16 (default) or float16 with round-to-nearest-even; the
+     result is returned as the raw uint16 bit patterns.
 """
 from __future__ import annotations
 
@@ -92,6 +92,16 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (numpy's conversion: round to nearest,
+    ties to even) and return the 16-bit patterns. Inputs must be finite and
+    below 65520 in magnitude."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.abs(x) < 65520.0):
+        raise ValueError("value out of float16 range")
+    return x.astype(np.float16).view(np.uint16)
+
+
 def _cube_bias(rng, heads, head_dim, latent, cube):
     """Per-head, per-key-cube bias a[h, cube] * g[h, :] laid out per token.
 
@@ -110,15 +120,20 @@ def _cube_bias(rng, heads, head_dim, latent, cube):
     return grid, g
 
 
-def make_inputs(w: Workload, seed: Optional[int] = None):
-    """Return (q, k, v) as uint16 bfloat16 bit arrays of shape [B, Hh, N, D]."""
+def make_inputs(w: Workload, seed: Optional[int] = None, dtype: str = "bf16"):
+    """Return (q, k, v) as uint16 bit arrays of shape [B, Hh, N, D] holding
+    bfloat16 (dtype "bf16") or float16 ("f16") values. Both types are drawn
+    from the same float32 numbers."""
+    if dtype not in ("bf16", "f16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
     shape = (w.batch, w.heads, w.seq_len, w.head_dim)
     q = rng.standard_normal(shape, dtype=np.float32)
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
     _modify(w, rng, k)
-    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    conv = f32_to_bf16_bits if dtype == "bf16" else f32_to_f16_bits
+    return conv(q), conv(k), conv(v)
 
 
 def _modify(w: Workload, rng, k: np.ndarray) -> None:
@@ -143,8 +158,10 @@ def custom_workload(name="custom", seed=0, batch=1, heads=2, head_dim=128,
                     tuple(cube), (topk,), prefix_len, modification)
 
 
-def bits_to_torch(bits: np.ndarray, device=None):
-    """View uint16 bfloat16 bit patterns as a torch.bfloat16 tensor."""
+def bits_to_torch(bits: np.ndarray, device=None, dtype: str = "bf16"):
+    """View uint16 bit patterns as a torch.bfloat16 ("bf16") or
+    torch.float16 ("f16") tensor."""
     import torch
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt)
     return t if device is None else t.to(device)

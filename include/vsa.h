@@ -20,7 +20,9 @@
  *   the kept cubes and of all prefix blocks.
  *
  * Data types and layouts
- *   q, k, v, o   bfloat16, element (b, h, n, d) at
+ *   q, k, v, o   bfloat16 or float16 (plan dtype; the user guide, section
+ *                "Verify routing and fallback": the Wan route takes FP16
+ *                or BF16), element (b, h, n, d) at
  *                b*stride_b + h*stride_h + n*stride_n + d   (elements);
  *                d is contiguous. q, k and v share one set of strides; o has
  *                its own. Base pointers and strides*2 must be multiples of
@@ -63,7 +65,7 @@ enum {
   VSA_ERR_TOPK = -2,         /* topk < 1 or topk > num_blocks (the user
                                 guide: top-k must be positive and may not
                                 exceed the block count)                     */
-  VSA_ERR_UNSUPPORTED = -3,  /* head_dim not 64 or 128, dtype not bf16,
+  VSA_ERR_UNSUPPORTED = -3,  /* head_dim not 64 or 128, dtype unknown,  
                                 cube volume > 1024, num_blocks > 16384      */
   VSA_ERR_ALIGN = -4,        /* pointer or stride not 16-byte aligned       */
   VSA_ERR_OVERFLOW = -5,     /* an element offset or a count would overflow
@@ -73,7 +75,10 @@ enum {
   VSA_ERR_LAUNCH = -7        /* a kernel launch reported an error           */
 };
 
-enum { VSA_DTYPE_BF16 = 0 };
+/* Element type of q, k, v and o. Softmax, row sums and the output
+   accumulator are float32 for both; P is rounded to the input type before
+   it multiplies V. */
+enum { VSA_DTYPE_BF16 = 0, VSA_DTYPE_F16 = 1 };
 
 /* What the caller asks for. All sizes in elements or tokens. */
 typedef struct vsa_problem {
@@ -84,7 +89,7 @@ typedef struct vsa_problem {
   int32_t cube[3];        /* (ct, ch, cw) block shape, each >= 1            */
   int32_t topk;           /* cubes kept per query block, 1..num_blocks       */
   int32_t prefix_len;     /* P >= 0 tokens before the grid, always kept      */
-  int32_t dtype;          /* VSA_DTYPE_BF16                                  */
+  int32_t dtype;          /* VSA_DTYPE_BF16 or VSA_DTYPE_F16                 */
   int64_t stride_b, stride_h, stride_n;        /* q, k, v strides (elements) */
   int64_t o_stride_b, o_stride_h, o_stride_n;  /* o strides (elements)       */
 } vsa_problem;
@@ -117,7 +122,7 @@ int vsa_plan(const vsa_problem* problem, vsa_plan_t* out);
  * works": the score matrix never leaves on-chip memory). Pools q over every
  * query block and k over every cube into the workspace, then scores every
  * query block against every cube and writes its topk cube ids, ascending,
- * to sel. q, k: device bf16 per the plan's strides. workspace: device,
+ * to sel. q, k: device bf16/fp16 (plan dtype) per the plan's strides. workspace: device,
  * >= plan->workspace_bytes, 256-byte aligned. sel: device int32,
  * plan->sel_elems. stream: hipStream_t or NULL. Asynchronous. */
 int vsa_select(const vsa_plan_t* plan, const void* q, const void* k,

@@ -51,13 +51,39 @@ import numpy as np
 
 
 # ----------------------------------------------------------------------------
-# bfloat16 decoding (exact)
+# 16-bit float decoding (exact)
 # ----------------------------------------------------------------------------
 
 def decode_bf16(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16) -> float64, exactly."""
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def decode_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE 754 binary16 bit patterns (uint16) -> float64, exactly, from the
+    format's definition: sign bit 15, biased exponent bits 14..10 (bias 15),
+    fraction bits 9..0; exponent 0 is subnormal (fraction * 2^-24), exponent
+    31 is infinity or NaN. (User guide, section "Verify routing and
+    fallback": the Wan route accepts FP16 as well as BF16.)"""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = np.ldexp(1.0 + f / 1024.0, (e - 15).astype(np.int64))
+    sub = np.ldexp(f, -24)
+    special = np.where(f == 0, np.inf, np.nan)
+    mag = np.where(e == 0, sub, np.where(e == 31, special, normal))
+    return sign * mag
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Bit patterns of the named 16-bit type ("bf16" or "f16") -> float64."""
+    if dtype == "bf16":
+        return decode_bf16(bits)
+    if dtype == "f16":
+        return decode_f16(bits)
+    raise ValueError(f"unknown dtype {dtype!r}")
 
 
 # ----------------------------------------------------------------------------

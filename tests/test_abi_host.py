@@ -42,6 +42,8 @@ def test_struct_layout_matches_c(tmp_path):
              'printf("%zu %zu\\n", sizeof(vsa_problem), sizeof(vsa_plan_t));']
     lines += [f'printf("p {f} %zu\\n", offsetof(vsa_problem, {f}));' for f in fields_p]
     lines += [f'printf("l {f} %zu\\n", offsetof(vsa_plan_t, {f}));' for f in fields_l]
+    consts = [n for n in dir(_lib) if re.fullmatch(r"VSA_(DTYPE|ERR)_\w+|VSA_OK", n)]
+    lines += [f'printf("c {n} %d\\n", (int){n});' for n in consts]
     lines.append("return 0;}")
     c = tmp_path / "layout.c"
     c.write_text("\n".join(lines))
@@ -54,6 +56,9 @@ def test_struct_layout_matches_c(tmp_path):
         if not line:
             continue
         kind, name, off = line.split()
+        if kind == "c":
+            assert getattr(_lib, name) == int(off), name
+            continue
         cls = _lib.VsaProblem if kind == "p" else _lib.VsaPlan
         assert getattr(cls, name).offset == int(off), name
 
@@ -121,15 +126,21 @@ def test_plan_status_codes(kw, status):
     assert _status(**kw) == status
 
 
-def test_plan_rejects_non_bf16_and_null():
+def test_plan_dtypes_and_null():
     pr = _lib.VsaProblem()
     out = _lib.VsaPlan()
     assert _lib.lib().vsa_plan(None, ctypes.byref(out)) == _lib.VSA_ERR_INVALID_ARG
     assert _lib.lib().vsa_plan(ctypes.byref(pr), None) == _lib.VSA_ERR_INVALID_ARG
     pl = vsa.plan(1, 2, 64, (8, 8, 8), (4, 4, 4), 4)
+    assert pl.dtype == _lib.VSA_DTYPE_BF16
+    assert vsa.plan(1, 2, 64, (8, 8, 8), (4, 4, 4), 4, dtype="f16").dtype == _lib.VSA_DTYPE_F16
+    with pytest.raises(ValueError):
+        vsa.plan(1, 2, 64, (8, 8, 8), (4, 4, 4), 4, dtype="f32")
     pr = pl.raw.p
-    pr.dtype = 7
-    assert _lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(out)) == _lib.VSA_ERR_UNSUPPORTED
+    for dt, want in ((_lib.VSA_DTYPE_F16, _lib.VSA_OK), (7, _lib.VSA_ERR_UNSUPPORTED),
+                     (-1, _lib.VSA_ERR_UNSUPPORTED)):
+        pr.dtype = dt
+        assert _lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(out)) == want
 
 
 def test_entry_points_check_arguments_before_touching_a_device():

@@ -49,8 +49,8 @@ def test_row_sums_read_distinct_p_registers(tmp_path):
     asm = _device_asm("attend.hip", tmp_path)
     checked = 0
     for blk in _blocks(asm):
-        srcs = [re.search(r"v_dot2c_f32_bf16_e32 v\d+, \S+, (v\d+)", i).group(1) for i in blk
-                if i.startswith("v_dot2c_f32_bf16")]
+        srcs = [re.search(r"v_dot2c_f32_b?f16_e32 v\d+, \S+, (v\d+)", i).group(1) for i in blk
+                if re.match(r"v_dot2c_f32_b?f16", i)]
         if len(srcs) >= 4:
             assert len(set(srcs)) == len(srcs), srcs
             checked += 1

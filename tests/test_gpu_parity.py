@@ -3,7 +3,8 @@
 Selection is compared with the oracle's float64 scores, bit-exact except
 for ids whose scores lie within 1e-6 of the row's k-th score. Outputs are
 compared with the oracle's dense-masked attention recomputed under the
-GPU's own selection: max-abs <= 2e-2 and relative L2 <= 1e-2.
+GPU's own selection: max-abs <= 2e-2 and relative L2 <= 1e-2 for bf16
+inputs, 4e-3 and 2e-3 for fp16 inputs.
 
 Small cases run the whole oracle; the full-size workloads check every
 selection row and the outputs of sampled query blocks (always including the
@@ -35,11 +36,11 @@ def _announce(msg):
     sys.stdout.flush()
 
 
-def _full_check(w, topk, heads=None, blocks_per_head=None):
+def _full_check(w, topk, heads=None, blocks_per_head=None, dtype="bf16"):
     _announce(f"{w.name}: B={w.batch} Hh={w.heads} D={w.head_dim} grid={w.latent} cube={w.cube} "
-              f"P={w.prefix_len} topk={topk}")
-    res = G.run_gpu(w, topk, _inputs(w))
-    g, qbar, kbar, scores = G.oracle_scores(w, res["bits"][0], res["bits"][1])
+              f"P={w.prefix_len} topk={topk} dtype={dtype}")
+    res = G.run_gpu(w, topk, _inputs(w, dtype), dtype=dtype)
+    g, qbar, kbar, scores = G.oracle_scores(w, res["bits"][0], res["bits"][1], dtype)
     # pooled means: float32 GPU vs float64 oracle
     np.testing.assert_allclose(res["qbar"], qbar, rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(res["kbar"], kbar, rtol=1e-5, atol=1e-5)
@@ -48,16 +49,16 @@ def _full_check(w, topk, heads=None, blocks_per_head=None):
     if heads is None:
         heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
     worst = G.check_outputs(w, g, res, heads, blocks_per_head)
-    _announce(f"{w.name}/topk{topk}: band rows {chk['band_rows']} of {chk['rows']}, "
+    _announce(f"{w.name}/topk{topk}/{dtype}: band rows {chk['band_rows']} of {chk['rows']}, "
               f"max_abs {worst['max_abs']:.3e} rel_l2 {worst['rel_l2']:.3e}")
-    assert worst["max_abs"] <= G.MAX_ABS
-    assert worst["rel_l2"] <= G.REL_L2
+    assert worst["max_abs"] <= G.TOL[dtype]["max_abs"]
+    assert worst["rel_l2"] <= G.TOL[dtype]["rel_l2"]
     return res, g
 
 
 @functools.lru_cache(maxsize=2)
-def _inputs(w):
-    return synthetic.make_inputs(w)
+def _inputs(w, dtype="bf16"):
+    return synthetic.make_inputs(w, dtype=dtype)
 
 
 SMALL = [
@@ -86,6 +87,15 @@ def test_small_case_full_oracle(case):
     w = synthetic.custom_workload(name, seed=zlib.crc32(name.encode()) & 0xFFFF, batch=B, heads=Hh, head_dim=D,
                                   latent=latent, cube=cube, topk=topk, prefix_len=P)
     _full_check(w, topk)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_case_full_oracle_f16(case):
+    """The same cases with fp16 q, k, v and output."""
+    name, B, Hh, D, latent, cube, topk, P = case
+    w = synthetic.custom_workload(name, seed=zlib.crc32(name.encode()) & 0xFFFF, batch=B, heads=Hh, head_dim=D,
+                                  latent=latent, cube=cube, topk=topk, prefix_len=P)
+    _full_check(w, topk, dtype="f16")
 
 
 def test_many_cubes_vector_select_path():
@@ -149,6 +159,42 @@ def test_constant_values_give_constant_output():
     _announce("constant V")
     res = G.run_gpu(w, 5, (q_b, k_b, v_b))
     assert np.max(np.abs(res["out"] - 1.0)) <= 2 ** -7
+
+
+def test_constant_values_give_constant_output_f16():
+    """V == 1 in fp16: O == 1 up to the fp16 rounding of P and of the
+    output (2^-10 covers both)."""
+    w = synthetic.custom_workload("ones_f16", seed=8, batch=1, heads=2, head_dim=128,
+                                  latent=(9, 10, 11), cube=(4, 8, 8), topk=5, prefix_len=40)
+    q_b, k_b, v_b = synthetic.make_inputs(w, dtype="f16")
+    v_b = np.full_like(v_b, 0x3C00)
+    _announce("constant V, fp16")
+    res = G.run_gpu(w, 5, (q_b, k_b, v_b), dtype="f16")
+    assert np.max(np.abs(res["out"] - 1.0)) <= 2 ** -10
+
+
+def test_f16_subnormal_and_large_values():
+    """fp16 inputs with subnormal entries (|x| < 2^-14) in q and v, and every
+    seventh key with 8 entries scaled by 64 (logits within a row spread
+    over tens of units), still match the oracle to the fp16 tolerance."""
+    w = synthetic.custom_workload("f16_range", seed=22, batch=1, heads=2, head_dim=64,
+                                  latent=(6, 7, 9), cube=(4, 4, 4), topk=4, prefix_len=10)
+    rng = np.random.default_rng(22)
+    N = w.seq_len
+    q = rng.standard_normal((1, 2, N, 64)).astype(np.float32)
+    k = rng.standard_normal((1, 2, N, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 2, N, 64)).astype(np.float32)
+    q[..., :8] *= np.float32(2.0 ** -17)         # subnormal in fp16
+    v[..., 8:16] *= np.float32(2.0 ** -18)
+    k[:, :, ::7, 16:24] *= np.float32(64.0)       # some keys with entries near 2^8..2^9
+    bits = tuple(synthetic.f32_to_f16_bits(x) for x in (q, k, v))
+    _announce("fp16 subnormal and large values")
+    res = G.run_gpu(w, 4, bits, dtype="f16")
+    g, qbar, kbar, scores = G.oracle_scores(w, bits[0], bits[1], "f16")
+    chk = O.check_selection(res["sel"], scores, 4, band=G.TIE_BAND)
+    assert chk["mismatch_rows"] == [], chk["mismatch_rows"][:10]
+    worst = G.check_outputs(w, g, res, [(0, 0), (0, 1)])
+    assert worst["max_abs"] <= G.TOL["f16"]["max_abs"] and worst["rel_l2"] <= G.TOL["f16"]["rel_l2"], worst
 
 
 def test_pool_centroid_through_workspace():
@@ -220,6 +266,11 @@ def test_workload_wan_sweep(topk):
     _full_check(w, topk, heads=[(0, 0), (0, 17)], blocks_per_head=5)
 
 
+def test_workload_wan_f16():
+    w = synthetic.WORKLOADS["wan"]
+    _full_check(w, 64, heads=[(0, 0), (0, 11), (0, 23)], blocks_per_head=6, dtype="f16")
+
+
 def test_workload_long720p():
     w = synthetic.WORKLOADS["long720p"]
     _full_check(w, 60, heads=[(0, 0), (0, 31)], blocks_per_head=12)
@@ -228,3 +279,8 @@ def test_workload_long720p():
 def test_workload_prefix():
     w = synthetic.WORKLOADS["prefix"]
     _full_check(w, 96, heads=[(0, 0), (1, 23)], blocks_per_head=12)
+
+
+def test_workload_prefix_f16():
+    w = synthetic.WORKLOADS["prefix"]
+    _full_check(w, 96, heads=[(0, 0), (1, 23)], blocks_per_head=12, dtype="f16")

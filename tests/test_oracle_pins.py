@@ -313,6 +313,32 @@ def test_decode_bf16_exact():
     assert O.decode_bf16(bits).tolist() == want
 
 
+def test_decode_f16_exact():
+    """Closed forms of IEEE binary16: one, a negative power of two, the
+    largest finite value (2 - 2^-10) * 2^15, the smallest normal 2^-14, the
+    smallest subnormal 2^-24, the largest subnormal (1 - 2^-10) * 2^-14,
+    1/3 rounded to 11 significant bits, signed zero and infinity."""
+    bits = np.array([0x3C00, 0xC000, 0x7BFF, 0x0400, 0x0001, 0x03FF, 0x3555, 0x8000, 0x7C00, 0xFC00],
+                    dtype=np.uint16)
+    want = [1.0, -2.0, 65504.0, 2.0 ** -14, 2.0 ** -24, (1 - 2.0 ** -10) * 2.0 ** -14,
+            1365.0 / 4096.0, -0.0, np.inf, -np.inf]
+    got = O.decode_f16(bits)
+    assert got.tolist() == want
+    assert np.signbit(got[7])
+    assert np.isnan(O.decode_f16(np.array([0x7E00, 0xFC01], dtype=np.uint16))).all()
+
+
+def test_decode_f16_matches_numpy_on_every_pattern():
+    """All 65536 patterns against numpy's own binary16 type (NaNs aside)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.decode_f16(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
 # ----------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ----------------------------------------------------------------------------
@@ -345,7 +371,23 @@ def _attend_wrong_scale(q, k, v, sel, g, query_blocks=None, return_rowsums=False
                                       query_blocks, return_rowsums)
 
 
+def _f16_bias_16(bits):
+    # exponent bias off by one
+    return O.__dict__["_orig_decode_f16"](bits) * 0.5
+
+
+def _f16_subnormals_as_normals(bits):
+    # exponent 0 given the implicit leading one
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    out = O.__dict__["_orig_decode_f16"](bits)
+    e0 = ((b >> 10) & 0x1F) == 0
+    out[e0] = np.where((b[e0] >> 15) & 1, -1.0, 1.0) * np.ldexp(1.0 + (b[e0] & 0x3FF) / 1024.0, -14)
+    return out
+
+
 @pytest.mark.parametrize("target,mutant,pin", [
+    ("decode_f16", _f16_bias_16, "f16_closed"),
+    ("decode_f16", _f16_subnormals_as_normals, "f16_numpy"),
     ("pool", _pool_zero_padded, "centroid"),
     ("select_topk", _select_ties_high, "ties"),
     ("kept_blocks", _kept_no_prefix, "brute_prefix"),
@@ -354,6 +396,7 @@ def _attend_wrong_scale(q, k, v, sel, g, query_blocks=None, return_rowsums=False
 ])
 def test_planted_mistakes(monkeypatch, target, mutant, pin):
     monkeypatch.setitem(O.__dict__, "_orig_attend", O.attend_dense_masked)
+    monkeypatch.setitem(O.__dict__, "_orig_decode_f16", O.decode_f16)
     monkeypatch.setattr(O, target, mutant)
     pins = {
         "centroid": lambda: test_pool_centroid((31, 22, 40), (4, 8, 8), 0),
@@ -361,6 +404,8 @@ def test_planted_mistakes(monkeypatch, target, mutant, pin):
         "brute_prefix": lambda: test_brute_force_per_token(*BRUTE_CASES[3]),
         "brute_padded": lambda: test_brute_force_per_token(*BRUTE_CASES[1]),
         "sdpa": lambda: test_all_blocks_equals_dense_sdpa((5, 6, 7), (2, 4, 4), 0, 32),
+        "f16_closed": test_decode_f16_exact,
+        "f16_numpy": test_decode_f16_matches_numpy_on_every_pattern,
     }
     with pytest.raises(AssertionError):
         pins[pin]()
