@@ -34,7 +34,14 @@ notes with its reason):
   R9  prefix tokens come first, form ceil(P / V) blocks of V = ct*ch*cw
       tokens (last one partial) and are kept by every query block in
       addition to its top-k video cubes;
-  R13 selection is per (batch, head).
+  R13 selection is per (batch, head);
+  R20 q and k/v may lie on different grids with different cube shapes
+      (fastbsa "Use": latent_shape_q / latent_shape_k, chunk_3d_shape_q /
+      chunk_3d_shape_k). Query blocks come from q's grid and cubes, key
+      blocks from k's; the prefix length is the same for both sequences and
+      each side cuts its prefix by its own cube volume;
+  R21 sparsity s (fastbsa "Use") keeps round(nb * (1 - s)) key cubes, ties
+      rounded up, clamped to 1..nb.
 
 Parity pins: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` against closed forms, the pages' numbers,
@@ -158,6 +165,16 @@ def routing_summary(g: Geometry, topk: int) -> dict:
     }
 
 
+def topk_for_sparsity(num_blocks: int, sparsity: float) -> int:
+    """Key cubes kept for a sparsity s in [0, 1) (fastbsa "Use"; R21): the
+    nearest integer to nb * (1 - s), halves rounded up, at least 1."""
+    s = float(sparsity)
+    if not (0.0 <= s < 1.0):
+        raise ValueError("sparsity must be in [0, 1)")
+    keep = math.floor(num_blocks * (1.0 - s) + 0.5 + 1e-9)
+    return int(min(max(keep, 1), num_blocks))
+
+
 def validate_topk(topk: int, num_blocks: int) -> None:
     """Top-k must be positive (user guide, "Alternative configuration
     formats") and at most the block count ("Wan top-k behavior")."""
@@ -222,15 +239,17 @@ def kept_blocks(sel_row: Iterable[int], g: Geometry) -> np.ndarray:
 def attend_dense_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                         sel: np.ndarray, g: Geometry,
                         query_blocks: Optional[Iterable[int]] = None,
-                        return_rowsums: bool = False):
+                        return_rowsums: bool = False, gk: Optional[Geometry] = None):
     """Exact softmax attention of each query token over the tokens of its
     query block's kept blocks, for one (batch, head).
 
-    q, k, v: [N, D] float64; sel: [nq, topk] video-cube ids.
-    L[n, m] = q_n . k_m * D ** -0.5 where block(m) is kept by block(n), else
-    -inf; P = softmax over m; O_n = sum_m P[n, m] v_m. Rows of blocks not in
-    ``query_blocks`` are left as NaN.
+    q: [Nq, D], k, v: [Nk, D] float64; sel: [nq, topk] video-cube ids of the
+    key grid. ``g`` partitions q; ``gk`` partitions k and v (default ``g``,
+    R20). L[n, m] = q_n . k_m * D ** -0.5 where key block(m) is kept by
+    query block(n), else -inf; P = softmax over m; O_n = sum_m P[n, m] v_m.
+    Rows of blocks not in ``query_blocks`` are left as NaN.
     """
+    gk = g if gk is None else gk
     N, D = q.shape
     scale = float(D) ** -0.5
     out = np.full((N, v.shape[1]), np.nan, dtype=np.float64)
@@ -238,7 +257,7 @@ def attend_dense_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     blocks = range(g.num_q_blocks) if query_blocks is None else query_blocks
     for i in blocks:
         rows = g.members[i]
-        keep = np.isin(g.block_of_token, kept_blocks(sel[i], g))
+        keep = np.isin(gk.block_of_token, kept_blocks(sel[i], gk))
         L = (q[rows] @ k.T) * scale
         L[:, ~keep] = -np.inf
         L -= L.max(axis=1, keepdims=True)
@@ -250,14 +269,16 @@ def attend_dense_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def forward_head(q, k, v, g: Geometry, topk: int,
-                 query_blocks: Optional[Iterable[int]] = None):
-    """Whole method for one (batch, head): returns (scores, sel, out)."""
+                 query_blocks: Optional[Iterable[int]] = None, gk: Optional[Geometry] = None):
+    """Whole method for one (batch, head): returns (scores, sel, out). ``gk``
+    is the key/value grid when it differs from the query grid ``g``."""
+    gk = g if gk is None else gk
     D = q.shape[-1]
     qbar = pool(q, g)
-    kbar = pool(k, g, video_only=True)
+    kbar = pool(k, gk, video_only=True)
     s = block_scores(qbar, kbar, D)
     sel = select_topk(s, topk)
-    out = attend_dense_masked(q, k, v, sel, g, query_blocks)
+    out = attend_dense_masked(q, k, v, sel, g, query_blocks, gk=gk)
     return s, sel, out
 
 
@@ -265,47 +286,59 @@ def forward_head(q, k, v, g: Geometry, topk: int,
 # Independent per-token brute force (tiny grids only; pure Python loops)
 # ----------------------------------------------------------------------------
 
-def brute_force_token(q, k, v, latent, cube, prefix_len: int, topk: int, n: int):
-    """Output row of token n, recomputed from scratch with Python loops.
+def brute_force_token(q, k, v, latent, cube, prefix_len: int, topk: int, n: int,
+                      latent_k=None, cube_k=None):
+    """Output row of query token n, recomputed from scratch with Python loops.
 
-    q, k, v: nested lists (or arrays) [N][D] for one head. The blocks are
-    found by walking the grid coordinates; the cube list is ordered by its
-    (bt, bh, bw) coordinates. Shares no code with the vectorised path.
+    q: nested list (or array) [Nq][D], k, v: [Nk][D] for one head; k and v
+    lie on ``latent_k`` cut into ``cube_k`` (default: q's grid and cube).
+    The blocks are found by walking the grid coordinates; the cube list is
+    ordered by its (bt, bh, bw) coordinates. Shares no code with the
+    vectorised path.
     """
-    T, H, W = latent
-    ct, ch, cw = cube
-    V = ct * ch * cw
     P = prefix_len
     D = len(q[0])
-    prefix_groups = {}
-    for tok in range(P):
-        prefix_groups.setdefault(tok // V, []).append(tok)
-    cubes = {}
-    for t in range(T):
-        for hh in range(H):
-            for w in range(W):
-                tok = P + (t * H + hh) * W + w
-                cubes.setdefault((t // ct, hh // ch, w // cw), []).append(tok)
-    cube_keys = sorted(cubes)
+
+    def blocks_of(lat, cb):
+        T, H, W = lat
+        ct, ch, cw = cb
+        V = ct * ch * cw
+        prefix_groups = {}
+        for tok in range(P):
+            prefix_groups.setdefault(tok // V, []).append(tok)
+        cubes = {}
+        for t in range(T):
+            for hh in range(H):
+                for w in range(W):
+                    tok = P + (t * H + hh) * W + w
+                    cubes.setdefault((t // ct, hh // ch, w // cw), []).append(tok)
+        return prefix_groups, cubes
+
+    q_prefix, q_cubes = blocks_of(latent, cube)
+    k_prefix, k_cubes = blocks_of(latent if latent_k is None else latent_k,
+                                  cube if cube_k is None else cube_k)
+    cube_keys = sorted(k_cubes)
 
     def mean(x, toks):
         return [sum(x[t][d] for t in toks) / len(toks) for d in range(D)]
 
+    T, H, W = latent
+    ct, ch, cw = cube
     if n < P:
-        my_tokens = prefix_groups[n // V]
+        my_tokens = q_prefix[n // (ct * ch * cw)]
     else:
         r = n - P
         t, hh, w = r // (H * W), (r // W) % H, r % W
-        my_tokens = cubes[(t // ct, hh // ch, w // cw)]
+        my_tokens = q_cubes[(t // ct, hh // ch, w // cw)]
     qm = mean(q, my_tokens)
     sc = []
     for key in cube_keys:
-        km = mean(k, cubes[key])
+        km = mean(k, k_cubes[key])
         sc.append(sum(qm[d] * km[d] for d in range(D)) / math.sqrt(D))
     ranked = sorted(range(len(cube_keys)), key=lambda j: (-sc[j], j))[:topk]
-    keys = [tok for grp in prefix_groups.values() for tok in grp]
+    keys = [tok for grp in k_prefix.values() for tok in grp]
     for j in ranked:
-        keys += cubes[cube_keys[j]]
+        keys += k_cubes[cube_keys[j]]
     logits = [sum(q[n][d] * k[m][d] for d in range(D)) / math.sqrt(D) for m in keys]
     mx = max(logits)
     ex = [math.exp(x - mx) for x in logits]

@@ -292,6 +292,66 @@ def test_brute_force_per_token(latent, cube, prefix, topk, D):
         np.testing.assert_allclose(out[n], bf, rtol=0, atol=1e-12)
 
 
+# q and k/v on different grids (fastbsa "Use": separate latent and chunk
+# shapes for q and k; R20): (latent_q, cube_q, latent_k, cube_k, prefix, topk, D)
+CROSS_CASES = [
+    ((4, 6, 5), (2, 2, 3), (3, 5, 7), (2, 4, 4), 0, 3, 8),    # partial cubes on both sides
+    ((2, 4, 4), (1, 2, 2), (4, 4, 4), (2, 2, 2), 6, 2, 8),    # prefix: 2 query, 1 key prefix blocks
+    ((3, 3, 3), (1, 1, 1), (3, 3, 3), (3, 3, 3), 0, 1, 8),    # one-token query blocks, one key cube
+]
+
+
+@pytest.mark.parametrize("lq,cq,lk,ck,prefix,topk,D", CROSS_CASES)
+def test_brute_force_cross_grids(lq, cq, lk, ck, prefix, topk, D):
+    gq, gk = O.geometry(lq, cq, prefix), O.geometry(lk, ck, prefix)
+    q = _rand((gq.seq_len, D), 17)
+    k, v = _rand((gk.seq_len, D), 18), _rand((gk.seq_len, D), 19)
+    _, sel, out = O.forward_head(q, k, v, gq, topk, gk=gk)
+    assert sel.shape == (gq.num_q_blocks, topk) and sel.max() < gk.num_blocks
+    ql, kl, vl = q.tolist(), k.tolist(), v.tolist()
+    for n in sorted(set(range(0, gq.seq_len, 5)) | {gq.seq_len - 1}):
+        bf = O.brute_force_token(ql, kl, vl, lq, cq, prefix, topk, n, latent_k=lk, cube_k=ck)
+        np.testing.assert_allclose(out[n], bf, rtol=0, atol=1e-12)
+
+
+def test_cross_grid_all_blocks_equals_dense_sdpa():
+    """Every key cube kept: dense attention of Nq queries over Nk keys."""
+    gq, gk = O.geometry((3, 4, 6), (2, 2, 4), 5), O.geometry((5, 3, 6), (4, 2, 2), 5)
+    D = 16
+    q = _rand((gq.seq_len, D), 21)
+    k, v = _rand((gk.seq_len, D), 22), _rand((gk.seq_len, D), 23)
+    _, _, out = O.forward_head(q, k, v, gq, gk.num_blocks, gk=gk)
+    np.testing.assert_allclose(out, _sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_one_token_query_blocks_score_each_token():
+    """Query cubes of one token: the pooled query is the token itself, so a
+    token's kept cubes are the top-k of q_n . kbar_j (closed form)."""
+    gq, gk = O.geometry((2, 3, 4), (1, 1, 1)), O.geometry((2, 3, 4), (1, 3, 2))
+    D = 8
+    q, k = _rand((gq.seq_len, D), 24), _rand((gk.seq_len, D), 25)
+    kbar = np.stack([k[m].mean(axis=0) for m in gk.members])
+    s, sel, _ = O.forward_head(q, k, k, gq, 2, gk=gk)
+    np.testing.assert_allclose(s, q @ kbar.T / math.sqrt(D), rtol=0, atol=1e-12)
+    want = np.sort(np.argsort(-(q @ kbar.T), axis=1, kind="stable")[:, :2], axis=1)
+    assert np.array_equal(sel, want)
+
+
+def test_topk_for_sparsity():
+    """fastbsa "Use" passes sparsity 0.9375: 1/16 of the cubes are kept
+    (R21: nearest integer, halves up, at least one, at most all)."""
+    assert O.topk_for_sparsity(960, 0.9375) == 60
+    assert O.topk_for_sparsity(624, 0.9375) == 39
+    assert O.topk_for_sparsity(120, 0.9375) == 8        # 7.5 rounds up
+    assert O.topk_for_sparsity(120, 0.9) == 12          # 12 up to float rounding of 1 - 0.9
+    assert O.topk_for_sparsity(120, 0.0) == 120
+    assert O.topk_for_sparsity(120, 0.999) == 1         # 0.12 -> at least one
+    assert O.topk_for_sparsity(7, 0.5) == 4             # 3.5 rounds up
+    for bad in (-0.1, 1.0, float("nan")):
+        with pytest.raises(ValueError):
+            O.topk_for_sparsity(120, bad)
+
+
 def test_shift_of_all_keys_changes_nothing():
     """Adding one vector b to every key adds q.b to a whole row of logits and
     qbar_i.b to a whole row of block scores: selection and output stay."""
@@ -365,10 +425,29 @@ def _scores_swapped(qbar, kbar, D):
     return np.swapaxes(np.matmul(qbar, np.swapaxes(kbar, -1, -2)), -1, -2) * D ** -0.5
 
 
-def _attend_wrong_scale(q, k, v, sel, g, query_blocks=None, return_rowsums=False):
+def _attend_wrong_scale(q, k, v, sel, g, query_blocks=None, return_rowsums=False, gk=None):
     # logits left unscaled (the head_dim ** -0.5 factor dropped)
     return O.__dict__["_orig_attend"](q * math.sqrt(q.shape[1]), k, v, sel, g,
-                                      query_blocks, return_rowsums)
+                                      query_blocks, return_rowsums, gk=gk)
+
+
+def _attend_query_prefix_count(q, k, v, sel, g, query_blocks=None, return_rowsums=False, gk=None):
+    # key blocks numbered with the query grid's prefix-block count
+    gk = g if gk is None else gk
+    out = np.full((q.shape[0], v.shape[1]), np.nan)
+    for i in (range(g.num_q_blocks) if query_blocks is None else query_blocks):
+        ids = list(range(g.num_prefix_blocks)) + [g.num_prefix_blocks + int(j) for j in sel[i]]
+        keep = np.isin(gk.block_of_token, ids)
+        L = (q[g.members[i]] @ k.T) / math.sqrt(q.shape[1])
+        L[:, ~keep] = -np.inf
+        Pm = np.exp(L - L.max(axis=1, keepdims=True))
+        out[g.members[i]] = (Pm / Pm.sum(axis=1, keepdims=True)) @ v
+    return out
+
+
+def _sparsity_floor(num_blocks, sparsity):
+    # truncation instead of rounding
+    return max(1, int(num_blocks * (1.0 - sparsity)))
 
 
 def _f16_bias_16(bits):
@@ -386,6 +465,8 @@ def _f16_subnormals_as_normals(bits):
 
 
 @pytest.mark.parametrize("target,mutant,pin", [
+    ("attend_dense_masked", _attend_query_prefix_count, "brute_cross_prefix"),
+    ("topk_for_sparsity", _sparsity_floor, "sparsity"),
     ("decode_f16", _f16_bias_16, "f16_closed"),
     ("decode_f16", _f16_subnormals_as_normals, "f16_numpy"),
     ("pool", _pool_zero_padded, "centroid"),
@@ -404,6 +485,8 @@ def test_planted_mistakes(monkeypatch, target, mutant, pin):
         "brute_prefix": lambda: test_brute_force_per_token(*BRUTE_CASES[3]),
         "brute_padded": lambda: test_brute_force_per_token(*BRUTE_CASES[1]),
         "sdpa": lambda: test_all_blocks_equals_dense_sdpa((5, 6, 7), (2, 4, 4), 0, 32),
+        "brute_cross_prefix": lambda: test_brute_force_cross_grids(*CROSS_CASES[1]),
+        "sparsity": test_topk_for_sparsity,
         "f16_closed": test_decode_f16_exact,
         "f16_numpy": test_decode_f16_matches_numpy_on_every_pattern,
     }
