@@ -11,7 +11,9 @@ load the library; the first call does, and raises if it is missing.
 
 q, k, v: bfloat16 or float16 CUDA (HIP) tensors [B, heads, N, head_dim] of
 one dtype, with the last dimension contiguous and N = prefix_len + T*H*W
-tokens in raster order. The output has their dtype.
+tokens in raster order. The output has their dtype. k and v may lie on a
+grid of their own (``latent_shape_k``, ``cube_shape_k``), as in fastbsa's
+``flash_attn_bsa_3d``, which this module also provides.
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ from typing import Optional, Sequence, Tuple
 from . import _lib
 from ._lib import VsaError
 
-__all__ = ["Plan", "VsaError", "plan", "plan_for", "select", "attend", "forward", "describe"]
+__all__ = ["Plan", "VsaError", "plan", "plan_for", "select", "attend", "forward", "flash_attn_bsa_3d",
+           "topk_for_sparsity", "describe"]
 
 
 class Plan:
@@ -34,21 +37,31 @@ class Plan:
         raw = self.__dict__["raw"]
         if hasattr(raw, name):
             v = getattr(raw, name)
-            return tuple(v) if name == "nblk" else v
+            return tuple(v) if name in ("nblk", "nblk_k") else v
         if hasattr(raw.p, name):
             v = getattr(raw.p, name)
-            return tuple(v) if name in ("latent", "cube") else v
+            return tuple(v) if name in ("latent", "cube", "latent_k", "cube_k") else v
         raise AttributeError(name)
 
-    def valid_counts(self):
-        """Valid token count of every query block (prefix blocks, then
-        cubes), from the plan's geometry. Host-side, numpy."""
+    @property
+    def kv_strides(self):
+        return (self.kv_stride_b, self.kv_stride_h, self.kv_stride_n)
+
+    def valid_counts(self, side: str = "q"):
+        """Valid token count of every block (prefix blocks, then cubes) of
+        q's grid (``side="q"``) or of k's (``"k"``). Host-side, numpy."""
         import numpy as np
-        T, H, W = self.latent
-        ct, ch, cw = self.cube
-        V, P = self.cube_volume, self.prefix_len
-        pre = [min(V, P - i * V) for i in range(self.num_prefix_blocks)]
-        ax = [np.minimum(c, L - np.arange(n) * c) for L, c, n in zip((T, H, W), (ct, ch, cw), self.nblk)]
+        if side == "q":
+            (T, H, W), (ct, ch, cw), nblk = self.latent, self.cube, self.nblk
+            V, Pb = self.cube_volume, self.num_prefix_blocks
+        elif side == "k":
+            (T, H, W), (ct, ch, cw), nblk = self.latent_k, self.cube_k, self.nblk_k
+            V, Pb = self.cube_volume_k, self.num_prefix_blocks_k
+        else:
+            raise ValueError("side must be 'q' or 'k'")
+        P = self.prefix_len
+        pre = [min(V, P - i * V) for i in range(Pb)]
+        ax = [np.minimum(c, L - np.arange(n) * c) for L, c, n in zip((T, H, W), (ct, ch, cw), nblk)]
         vid = (ax[0][:, None, None] * ax[1][None, :, None] * ax[2][None, None, :]).reshape(-1)
         return np.concatenate([np.array(pre, dtype=np.int64), vid.astype(np.int64)])
 
@@ -61,12 +74,16 @@ _DTYPES = {"bf16": _lib.VSA_DTYPE_BF16, "f16": _lib.VSA_DTYPE_F16}
 
 def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Sequence[int], topk: int,
          prefix_len: int = 0, strides: Optional[Sequence[int]] = None,
-         o_strides: Optional[Sequence[int]] = None, dtype: str = "bf16") -> Plan:
+         o_strides: Optional[Sequence[int]] = None, dtype: str = "bf16",
+         latent_k: Optional[Sequence[int]] = None, cube_k: Optional[Sequence[int]] = None,
+         kv_strides: Optional[Sequence[int]] = None) -> Plan:
     """Validate a problem and derive its geometry (vsa_plan). ``strides``
-    are the (b, h, n) element strides shared by q, k and v; the default is
-    a contiguous [B, heads, N, head_dim] layout. ``o_strides`` default to
-    ``strides``. ``dtype`` is "bf16" or "f16", the element type of q, k, v
-    and o."""
+    are the (b, h, n) element strides of q (and of k and v unless
+    ``kv_strides`` is given); the default is a contiguous
+    [B, heads, N, head_dim] layout. ``o_strides`` default to ``strides``.
+    ``dtype`` is "bf16" or "f16", the element type of q, k, v and o.
+    ``latent_k`` and ``cube_k`` put k and v on a grid of their own (default:
+    q's); ``kv_strides`` then default to a contiguous layout of that grid."""
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be one of {sorted(_DTYPES)}, got {dtype!r}")
     N = int(prefix_len) + int(latent[0]) * int(latent[1]) * int(latent[2])
@@ -74,6 +91,14 @@ def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Seq
         strides = (heads * N * head_dim, N * head_dim, head_dim)
     if o_strides is None:
         o_strides = strides
+    latent_k = tuple(latent) if latent_k is None else tuple(latent_k)
+    cube_k = tuple(cube) if cube_k is None else tuple(cube_k)
+    if kv_strides is None:
+        if latent_k == tuple(latent):
+            kv_strides = strides
+        else:
+            Nk = int(prefix_len) + int(latent_k[0]) * int(latent_k[1]) * int(latent_k[2])
+            kv_strides = (heads * Nk * head_dim, Nk * head_dim, head_dim)
     pr = _lib.VsaProblem()
     pr.batch, pr.heads, pr.head_dim = int(batch), int(heads), int(head_dim)
     pr.latent[:] = [int(x) for x in latent]
@@ -81,6 +106,9 @@ def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Seq
     pr.topk, pr.prefix_len, pr.dtype = int(topk), int(prefix_len), _DTYPES[dtype]
     pr.stride_b, pr.stride_h, pr.stride_n = (int(s) for s in strides)
     pr.o_stride_b, pr.o_stride_h, pr.o_stride_n = (int(s) for s in o_strides)
+    pr.latent_k[:] = [int(x) for x in latent_k]
+    pr.cube_k[:] = [int(x) for x in cube_k]
+    pr.kv_stride_b, pr.kv_stride_h, pr.kv_stride_n = (int(s) for s in kv_strides)
     raw = _lib.VsaPlan()
     _lib.check(_lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(raw)), "vsa_plan")
     return Plan(raw)
@@ -107,15 +135,19 @@ def _check_qkv(t, name, shape, strides, dtype):
 
 
 def plan_for(q, latent: Sequence[int], cube: Sequence[int], topk: int, prefix_len: int = 0,
-             out=None) -> Plan:
-    """Plan from q's shape, strides and dtype (and out's strides, if given)."""
+             out=None, k=None, latent_k: Optional[Sequence[int]] = None,
+             cube_k: Optional[Sequence[int]] = None) -> Plan:
+    """Plan from q's shape, strides and dtype (out's strides and k's, if
+    given; k and v must share strides)."""
     import torch
     B, Hh, N, D = q.shape
     o_strides = out.stride()[:3] if out is not None else q.stride()[:3]
+    kv_strides = k.stride()[:3] if k is not None else None
     names = {torch.bfloat16: "bf16", torch.float16: "f16"}
     if q.dtype not in names:
         raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
-    return plan(B, Hh, D, latent, cube, topk, prefix_len, q.stride()[:3], o_strides, names[q.dtype])
+    return plan(B, Hh, D, latent, cube, topk, prefix_len, q.stride()[:3], o_strides, names[q.dtype],
+                latent_k, cube_k, kv_strides)
 
 
 def _stream_ptr(device):
@@ -130,9 +162,10 @@ def select(pl: Plan, q, k, workspace=None, sel=None):
     import torch
     shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
     strides = (pl.stride_b, pl.stride_h, pl.stride_n)
+    kshape = (pl.batch, pl.heads, pl.seq_len_k, pl.head_dim)
     dt = _torch_dtype(pl)
     _check_qkv(q, "q", shape, strides, dt)
-    _check_qkv(k, "k", shape, strides, dt)
+    _check_qkv(k, "k", kshape, pl.kv_strides, dt)
     dev = q.device
     if workspace is None:
         workspace = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
@@ -154,9 +187,11 @@ def attend(pl: Plan, q, k, v, sel, out=None):
     import torch
     shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
     strides = (pl.stride_b, pl.stride_h, pl.stride_n)
+    kshape = (pl.batch, pl.heads, pl.seq_len_k, pl.head_dim)
     dt = _torch_dtype(pl)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_qkv(t, n, shape, strides, dt)
+    _check_qkv(q, "q", shape, strides, dt)
+    for t, n in ((k, "k"), (v, "v")):
+        _check_qkv(t, n, kshape, pl.kv_strides, dt)
     dev = q.device
     if out is None:
         out = torch.empty_strided(shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n, 1),
@@ -173,12 +208,43 @@ def attend(pl: Plan, q, k, v, sel, out=None):
 
 
 def forward(q, k, v, latent_shape: Sequence[int], cube_shape: Sequence[int], topk: int,
-            prefix_len: int = 0, out=None, return_sel: bool = False):
-    """Select then attend on the current stream. Returns out (and sel)."""
-    pl = plan_for(q, latent_shape, cube_shape, topk, prefix_len, out)
+            prefix_len: int = 0, out=None, return_sel: bool = False,
+            latent_shape_k: Optional[Sequence[int]] = None, cube_shape_k: Optional[Sequence[int]] = None):
+    """Select then attend on the current stream. Returns out (and sel).
+    ``latent_shape_k`` / ``cube_shape_k`` give k and v a grid of their own."""
+    pl = plan_for(q, latent_shape, cube_shape, topk, prefix_len, out, k, latent_shape_k, cube_shape_k)
     sel, _ = select(pl, q, k)
     out = attend(pl, q, k, v, sel, out)
     return (out, sel) if return_sel else out
+
+
+def topk_for_sparsity(num_blocks: int, sparsity: float) -> int:
+    """Key cubes kept for a sparsity in [0, 1) (vsa_topk_for_sparsity): the
+    nearest integer to num_blocks * (1 - sparsity), halves up, at least 1."""
+    r = _lib.lib().vsa_topk_for_sparsity(int(num_blocks), float(sparsity))
+    if r < 0:
+        raise VsaError(r, "vsa_topk_for_sparsity")
+    return r
+
+
+def flash_attn_bsa_3d(q, k, v, latent_shape_q: Sequence[int], latent_shape_k: Sequence[int],
+                      sparsity: Optional[float] = None, chunk_3d_shape_q: Sequence[int] = (4, 4, 4),
+                      chunk_3d_shape_k: Sequence[int] = (4, 4, 4), topk: Optional[int] = None,
+                      prefix_len: int = 0, out=None):
+    """fastbsa's call (package page, section "Use"): q on ``latent_shape_q``
+    cut into ``chunk_3d_shape_q`` chunks, k and v on ``latent_shape_k`` cut
+    into ``chunk_3d_shape_k``; each query chunk keeps the top (1 - sparsity)
+    of the key chunks (or ``topk`` of them). Layout [B, heads, N, head_dim]
+    as in ``forward``. Returns the output."""
+    if (sparsity is None) == (topk is None):
+        raise ValueError("give exactly one of sparsity and topk")
+    if topk is None:
+        nb_k = 1
+        for L, c in zip(latent_shape_k, chunk_3d_shape_k):
+            nb_k *= -(-int(L) // int(c))
+        topk = topk_for_sparsity(nb_k, sparsity)
+    return forward(q, k, v, latent_shape_q, chunk_3d_shape_q, topk, prefix_len, out,
+                   latent_shape_k=latent_shape_k, cube_shape_k=chunk_3d_shape_k)
 
 
 def describe(pl: Plan) -> str:

@@ -18,8 +18,8 @@ VSA_ERR_LAUNCH = -7
 VSA_DTYPE_BF16 = 0
 VSA_DTYPE_F16 = 1
 
-EXPORTED = ("vsa_plan", "vsa_select", "vsa_attend", "vsa_forward", "vsa_describe",
-            "vsa_status_str")
+EXPORTED = ("vsa_plan", "vsa_topk_for_sparsity", "vsa_select", "vsa_attend", "vsa_forward",
+            "vsa_describe", "vsa_status_str")
 
 
 class VsaProblem(ctypes.Structure):
@@ -29,6 +29,8 @@ class VsaProblem(ctypes.Structure):
         ("topk", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
         ("o_stride_b", ctypes.c_int64), ("o_stride_h", ctypes.c_int64), ("o_stride_n", ctypes.c_int64),
+        ("latent_k", ctypes.c_int32 * 3), ("cube_k", ctypes.c_int32 * 3),
+        ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_n", ctypes.c_int64),
     ]
 
 
@@ -43,6 +45,8 @@ class VsaPlan(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("select_rows", ctypes.c_int32), ("attend_variant", ctypes.c_int32),
         ("attend_tiles", ctypes.c_int32),
+        ("nblk_k", ctypes.c_int32 * 3), ("num_prefix_blocks_k", ctypes.c_int32),
+        ("cube_volume_k", ctypes.c_int32), ("seq_len_k", ctypes.c_int64),
     ]
 
 
@@ -68,6 +72,8 @@ def lib() -> ctypes.CDLL:
         vp = ctypes.c_void_p
         L.vsa_plan.argtypes = [ctypes.POINTER(VsaProblem), ctypes.POINTER(VsaPlan)]
         L.vsa_plan.restype = ctypes.c_int
+        L.vsa_topk_for_sparsity.argtypes = [ctypes.c_int32, ctypes.c_double]
+        L.vsa_topk_for_sparsity.restype = ctypes.c_int
         L.vsa_select.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp]
         L.vsa_select.restype = ctypes.c_int
         L.vsa_attend.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp, vp]

@@ -51,8 +51,41 @@ int check_plan(const vsa_plan_t* plan) {
       fresh.seq_len == plan->seq_len && fresh.workspace_bytes == plan->workspace_bytes &&
       fresh.kbar_offset == plan->kbar_offset && fresh.sel_elems == plan->sel_elems &&
       fresh.scale == plan->scale && fresh.select_rows == plan->select_rows &&
-      fresh.attend_variant == plan->attend_variant && fresh.attend_tiles == plan->attend_tiles;
+      fresh.attend_variant == plan->attend_variant && fresh.attend_tiles == plan->attend_tiles &&
+      fresh.nblk_k[0] == plan->nblk_k[0] && fresh.nblk_k[1] == plan->nblk_k[1] &&
+      fresh.nblk_k[2] == plan->nblk_k[2] && fresh.num_prefix_blocks_k == plan->num_prefix_blocks_k &&
+      fresh.cube_volume_k == plan->cube_volume_k && fresh.seq_len_k == plan->seq_len_k &&
+      std::memcmp(&fresh.p, &plan->p, sizeof(vsa_problem)) == 0;
   return same ? VSA_OK : VSA_ERR_INVALID_ARG;
+}
+
+uint64_t magic(int64_t d) { return ((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d; }
+
+VsaGrid make_grid(const int32_t* latent, const int32_t* cube, const int32_t* nblk, int32_t P, int32_t V,
+                  int32_t Pb) {
+  VsaGrid g;
+  std::memset(&g, 0, sizeof(g));
+  g.T = latent[0];
+  g.H = latent[1];
+  g.W = latent[2];
+  g.ct = cube[0];
+  g.ch = cube[1];
+  g.cw = cube[2];
+  g.nT = nblk[0];
+  g.nH = nblk[1];
+  g.nW = nblk[2];
+  g.P = P;
+  g.V = V;
+  g.Pb = Pb;
+  g.nb = g.nT * g.nH * g.nW;
+  g.magic_nW = magic(g.nW);
+  g.magic_nH = magic(g.nH);
+  const int64_t tail_h = g.H - (int64_t)(g.nH - 1) * g.ch, tail_w = g.W - (int64_t)(g.nW - 1) * g.cw;
+  const int64_t ehs[2] = {g.ch, tail_h}, ews[2] = {g.cw, tail_w};
+  for (int iw = 0; iw < 2; ++iw) g.magic_ew[iw] = magic(ews[iw]);
+  for (int ih = 0; ih < 2; ++ih)
+    for (int iw = 0; iw < 2; ++iw) g.magic_ehw[2 * ih + iw] = magic(ehs[ih] * ews[iw]);
+  return g;
 }
 
 VsaArgs make_args(const vsa_plan_t& pl) {
@@ -62,39 +95,24 @@ VsaArgs make_args(const vsa_plan_t& pl) {
   a.B = p.batch;
   a.Hh = p.heads;
   a.D = p.head_dim;
-  a.T = p.latent[0];
-  a.H = p.latent[1];
-  a.W = p.latent[2];
-  a.ct = p.cube[0];
-  a.ch = p.cube[1];
-  a.cw = p.cube[2];
-  a.nT = pl.nblk[0];
-  a.nH = pl.nblk[1];
-  a.nW = pl.nblk[2];
-  a.P = p.prefix_len;
-  a.V = pl.cube_volume;
-  a.Pb = pl.num_prefix_blocks;
-  a.nb = pl.num_blocks;
+  a.gq = make_grid(p.latent, p.cube, pl.nblk, p.prefix_len, pl.cube_volume, pl.num_prefix_blocks);
+  a.gk = make_grid(p.latent_k, p.cube_k, pl.nblk_k, p.prefix_len, pl.cube_volume_k, pl.num_prefix_blocks_k);
   a.nq = pl.num_q_blocks;
+  a.nb = pl.num_blocks;
   a.topk = p.topk;
   a.sb = p.stride_b;
   a.sh = p.stride_h;
   a.sn = (int32_t)p.stride_n;
+  a.ksb = p.kv_stride_b;
+  a.ksh = p.kv_stride_h;
+  a.ksn = (int32_t)p.kv_stride_n;
   a.osb = p.o_stride_b;
   a.osh = p.o_stride_h;
   a.osn = (int32_t)p.o_stride_n;
   a.scale_log2e = pl.scale * 1.4426950408889634f;
   a.select_rows = pl.select_rows;
   a.tiles = pl.attend_tiles;
-  a.magic_nW = ((1ull << 32) + (uint64_t)a.nW - 1) / (uint64_t)a.nW;
-  a.magic_nH = ((1ull << 32) + (uint64_t)a.nH - 1) / (uint64_t)a.nH;
   a.f16 = p.dtype == VSA_DTYPE_F16;
-  auto magic = [](int64_t d) { return ((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d; };
-  const int64_t tail_h = a.H - (int64_t)(a.nH - 1) * a.ch, tail_w = a.W - (int64_t)(a.nW - 1) * a.cw;
-  const int64_t ehs[2] = {a.ch, tail_h}, ews[2] = {a.cw, tail_w};
-  for (int iw = 0; iw < 2; ++iw) a.magic_ew[iw] = magic(ews[iw]);
-  for (int ih = 0; ih < 2; ++ih)
-    for (int iw = 0; iw < 2; ++iw) a.magic_ehw[2 * ih + iw] = magic(ehs[ih] * ews[iw]);
   return a;
 }
 

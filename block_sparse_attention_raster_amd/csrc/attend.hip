@@ -15,10 +15,12 @@
 // block tokens are rows p*V + k. Both query rows and key tiles walk this
 // compact numbering, so a block of n tokens fills floor(n/64) whole key
 // tiles and at most one tail tile, whose slots past n load the block's first
-// row (finite data) and are masked to -inf. For whole cubes the workgroup
-// tabulates each k's row offset (tt*H + hh)*W + ww from the cube's first
-// token at start-up (one LDS read per row); partial cubes unravel k with
-// multiply-high divisions by eh*ew and ew.
+// row (finite data) and are masked to -inf. For whole key cubes the
+// workgroup tabulates each k's row offset (tt*H + hh)*W + ww from the cube's
+// first token at start-up (one LDS read per row); partial cubes, and query
+// rows, unravel k with multiply-high divisions by eh*ew and ew. Query blocks
+// follow q's grid and cube shape, key blocks k's (the two differ when q and
+// k/v lie on different grids: fastbsa package page, section "Use").
 //
 // Data movement. K and V tiles go from HBM straight into LDS with 16-byte
 // global_load_lds (no registers), NSTAGE tiles deep; each wave issues its
@@ -139,11 +141,11 @@ struct Blk {
   bool full;        // a whole cube (n == V) or a whole prefix block
 };
 
-__device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk, int32_t kt) {
+__device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int32_t kt) {
   Blk d;
-  if (blk < a.Pb) {
-    const int32_t s = blk * a.V;
-    const int32_t n = min(a.V, a.P - s);
+  if (blk < g.Pb) {
+    const int32_t s = blk * g.V;
+    const int32_t n = min(g.V, g.P - s);
     d.base = s;
     d.n = n;
     d.ntiles = (n + kt - 1) / kt;
@@ -151,26 +153,26 @@ __device__ __forceinline__ Blk describe_block(const VsaArgs& a, int32_t blk, int
     d.ehw = n;
     d.mw = d.mhw = 0;
     d.prefix = true;
-    d.full = n == a.V;
+    d.full = n == g.V;
     return d;
   }
-  const int32_t c = blk - a.Pb;
-  const int32_t rest = fast_div(c, a.magic_nW);
-  const int32_t bw = c - rest * a.nW;
-  const int32_t bt = fast_div(rest, a.magic_nH);
-  const int32_t bh = rest - bt * a.nH;
-  const int32_t t0 = bt * a.ct, h0 = bh * a.ch, w0 = bw * a.cw;
-  const int32_t et = min(a.ct, a.T - t0), eh = min(a.ch, a.H - h0), ew = min(a.cw, a.W - w0);
-  const int ih = eh != a.ch, iw = ew != a.cw;
-  d.base = a.P + (t0 * a.H + h0) * a.W + w0;
+  const int32_t c = blk - g.Pb;
+  const int32_t rest = fast_div(c, g.magic_nW);
+  const int32_t bw = c - rest * g.nW;
+  const int32_t bt = fast_div(rest, g.magic_nH);
+  const int32_t bh = rest - bt * g.nH;
+  const int32_t t0 = bt * g.ct, h0 = bh * g.ch, w0 = bw * g.cw;
+  const int32_t et = min(g.ct, g.T - t0), eh = min(g.ch, g.H - h0), ew = min(g.cw, g.W - w0);
+  const int ih = eh != g.ch, iw = ew != g.cw;
+  d.base = g.P + (t0 * g.H + h0) * g.W + w0;
   d.n = et * eh * ew;
   d.ntiles = (d.n + kt - 1) / kt;
   d.ew = ew;
   d.ehw = eh * ew;
-  d.mw = a.magic_ew[iw];
-  d.mhw = a.magic_ehw[2 * ih + iw];
+  d.mw = g.magic_ew[iw];
+  d.mhw = g.magic_ehw[2 * ih + iw];
   d.prefix = false;
-  d.full = d.n == a.V;
+  d.full = d.n == g.V;
   return d;
 }
 
@@ -225,7 +227,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   unsigned char* kst = smem;                              // [NSTAGE][TILE_BYTES]
   unsigned char* vst = smem + NSTAGE * TILE_BYTES;        // [NSTAGE][TILE_BYTES]
   int32_t* srel = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);  // [V]
-  int32_t* ssel = srel + a.V;   // [topk] kept cubes, when topk <= VSA_ATTEND_SEL_LDS
+  const VsaGrid& gk = a.gk;     // key/value side
+  int32_t* ssel = srel + gk.V;  // [topk] kept cubes, when topk <= VSA_ATTEND_SEL_LDS
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
   // id is remapped to give each XCD a contiguous range of (head, block) work.
@@ -239,19 +242,19 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int qblk = bid % a.nq;
   const int bh = bid / a.nq;
   const int b = bh / a.Hh, h = bh - b * a.Hh;
-  const Blk qd = describe_block(a, qblk, KT);
+  const Blk qd = describe_block(a.gq, qblk, KT);
   const int slot0 = tile * RW;
   if (slot0 >= qd.n) return;
 
   const int tid = threadIdx.x;
-  {
-    const int chw = a.ch * a.cw;
-    for (int s = tid; s < a.V; s += NW * 64) {
+  {  // row offsets of a whole key cube's slots from its first row
+    const int chw = gk.ch * gk.cw;
+    for (int s = tid; s < gk.V; s += NW * 64) {
       const int tt = s / chw;
       const int rem = s - tt * chw;
-      const int hh = rem / a.cw;
-      const int ww = rem - hh * a.cw;
-      srel[s] = (tt * a.H + hh) * a.W + ww;
+      const int hh = rem / gk.cw;
+      const int ww = rem - hh * gk.cw;
+      srel[s] = (tt * gk.H + hh) * gk.W + ww;
     }
   }
   const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
@@ -264,16 +267,16 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   }
   __syncthreads();
 
-  const int64_t in_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const __bf16* qh = q + in_off;
-  const __bf16* kh = k + in_off;
-  const __bf16* vh = v + in_off;
+  const __bf16* qh = q + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const int64_t kv_off = (int64_t)b * a.ksb + (int64_t)h * a.ksh;
+  const __bf16* kh = k + kv_off;
+  const __bf16* vh = v + kv_off;
   __bf16* oh = o + (int64_t)b * a.osb + (int64_t)h * a.osh;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // token row of compact index k < d.n of block d
+  // token row of compact index k < d.n of key block d
   auto compact_row = [&](const Blk& d, int k) -> int {
     if (d.prefix) return d.base + k;
     if (d.full) return d.base + srel[k];
@@ -281,7 +284,17 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     const int r = k - tt * d.ehw;
     const int hh = fast_div(r, d.mw);
     const int ww = r - hh * d.ew;
-    return d.base + (tt * a.H + hh) * a.W + ww;
+    return d.base + (tt * gk.H + hh) * gk.W + ww;
+  };
+  // token row of compact index k < d.n of the query block (q's grid; every
+  // video cube, whole or partial, carries its extents' division magics)
+  auto query_row = [&](const Blk& d, int k) -> int {
+    if (d.prefix) return d.base + k;
+    const int tt = fast_div(k, d.mhw);
+    const int r = k - tt * d.ehw;
+    const int hh = fast_div(r, d.mw);
+    const int ww = r - hh * d.ew;
+    return d.base + (tt * a.gq.H + hh) * a.gq.W + ww;
   };
 
   // ---- Q rows of this wave, in MFMA B-operand layout
@@ -290,7 +303,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int slot = slot0 + wave * 32 * QB + qb * 32 + l32;
-    qrow[qb] = slot < qd.n ? compact_row(qd, slot) : -1;
+    qrow[qb] = slot < qd.n ? query_row(qd, slot) : -1;
     if (qrow[qb] >= 0) {
       const __bf16* src = qh + (int64_t)qrow[qb] * a.sn + 8 * g;
 #pragma unroll
@@ -320,17 +333,17 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   }
 
   // ---- kept-block walk (issue side)
-  const int nkept = a.Pb + a.topk;
+  const int nkept = gk.Pb + a.topk;
   auto kept_block = [&](int i) -> int {
-    if (i < a.Pb) return i;
-    if (sel_lds) return a.Pb + __builtin_amdgcn_readfirstlane(ssel[i - a.Pb]);
-    int c = selrow[i - a.Pb];
+    if (i < gk.Pb) return i;
+    if (sel_lds) return gk.Pb + __builtin_amdgcn_readfirstlane(ssel[i - gk.Pb]);
+    int c = selrow[i - gk.Pb];
     c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
-    return a.Pb + c;
+    return gk.Pb + c;
   };
   int ibi = 0, ikt = 0;
-  Blk kd = describe_block(a, kept_block(0), KT);
-  const uint32_t last_row = (uint32_t)(a.P + a.T * a.H * a.W - 1);  // bound of every load row
+  Blk kd = describe_block(gk, kept_block(0), KT);
+  const uint32_t last_row = (uint32_t)(gk.P + gk.T * gk.H * gk.W - 1);  // bound of every k/v load row
 
   // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
   // for s = wave*SPW + j: key row (s*64 + lane)/CPR, chunk position
@@ -355,7 +368,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
       const bool valid = key < nleft;
       const int row = valid ? compact_row(kd, t * KT + key) : kd.base;
-      const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.sn * 2u;
+      const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.ksn * 2u;
       const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
       dma16(kh, ro + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
       if (!PIPE || nleft >= KT) {
@@ -371,7 +384,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     if (ikt >= kd.ntiles) {
       ikt = 0;
       ++ibi;
-      if (ibi < nkept) kd = describe_block(a, kept_block(ibi), KT);
+      if (ibi < nkept) kd = describe_block(gk, kept_block(ibi), KT);
     }
     return m;
   };
@@ -397,14 +410,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     uint32_t ko[SPW];              // K byte offsets from kh
     const unsigned char* va[SPW];  // V source addresses (zero row for tail slots)
   };
-  const int chw = a.ch * a.cw;
+  const int chw = gk.ch * gk.cw;
   const bool fastshape = (KT % chw) == 0;
-  const int64_t tile_rows = (int64_t)(KT / chw) * a.H * a.W;
+  const int64_t tile_rows = (int64_t)(KT / chw) * gk.H * gk.W;
   int srk[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int key = ((wave * SPW + j) * 64 + lane) / CPR;
-    srk[j] = (PIPE && fastshape && key < a.V) ? srel[key] : 0;
+    srk[j] = (PIPE && fastshape && key < gk.V) ? srel[key] : 0;
   }
   // describes the walker's current tile as ring slot AHEAD, then advances
   auto spec = [&](Spec& sp, uint64_t& m, bool& e) {
@@ -426,7 +439,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       if (ikt >= kd.ntiles) {
         ikt = 0;
         ++ibi;
-        if (ibi < nkept) kd = describe_block(a, kept_block(ibi), KT);
+        if (ibi < nkept) kd = describe_block(gk, kept_block(ibi), KT);
       }
     }
   };
@@ -448,13 +461,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     int m_pre = -(int)(sp.mode == 1), m_whole = -(int)(sp.mode == 0), m_val = -(int)valid;
     int m_none = -(int)(sp.mode == 3);
     asm volatile("" : "+v"(m_pre), "+v"(m_whole), "+v"(m_val), "+v"(m_none));
-    int row = sp.base + (tt * a.H + hh) * a.W + ww;
+    int row = sp.base + (tt * gk.H + hh) * gk.W + ww;
     row = (row & ~m_pre) | ((sp.base + kc) & m_pre);
     row = (row & ~m_whole) | ((sp.base + sp.trow + srk[j]) & m_whole);
     row = (row & m_val) | (sp.base & ~m_val);
     row &= ~m_none;
     // guard: never address past the last token row
-    const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.sn * 2u;
+    const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.ksn * 2u;
     const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
     pd.ko[j] = ro + (uint32_t)((cp ^ (key & KSWZ)) * 16);
     const uint64_t vv = (uint64_t)reinterpret_cast<uintptr_t>(vh) + ro + vo;
@@ -891,7 +904,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE, bool F16>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
-  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.V * 4 +
+  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.gk.V * 4 +
                     (a.topk <= VSA_ATTEND_SEL_LDS ? (size_t)a.topk * 4 : 0);
   if (lds > 65536) {
     static bool raised = false;  // benign race: the attribute call is idempotent

@@ -8,7 +8,9 @@
 // "Wan top-k behavior"), top-k must be positive and not above the block
 // count (sections "Alternative configuration formats" and "Wan top-k
 // behavior"), and prefix blocks have the cube's token count (section
-// "Choose top-k": 64-token blocks that keep all prefix blocks).
+// "Choose top-k": 64-token blocks that keep all prefix blocks). q and k/v may
+// lie on different grids with different cube shapes, and a sparsity maps to
+// a top-k (the "fastbsa" package page, section "Use").
 
 #include <cstdint>
 #include <cstdio>
@@ -34,65 +36,119 @@ bool span_fits(int64_t B, int64_t Hh, int64_t N, int64_t D, int64_t sb, int64_t 
   return (B - 1) * sb + (Hh - 1) * sh + (N - 1) * sn + D < lim;
 }
 
+// One side's grid cut into blocks (q's or k/v's).
+struct Side {
+  int64_t T, H, W, ct, ch, cw;
+  int64_t nT, nH, nW, V, nb, Pb, N;
+};
+
+int derive_side(const int32_t* latent, const int32_t* cube, int64_t P, Side& s) {
+  s.T = latent[0];
+  s.H = latent[1];
+  s.W = latent[2];
+  s.ct = cube[0];
+  s.ch = cube[1];
+  s.cw = cube[2];
+  if (s.T < 1 || s.H < 1 || s.W < 1 || s.ct < 1 || s.ch < 1 || s.cw < 1) return VSA_ERR_INVALID_ARG;
+  s.nT = ceil_div(s.T, s.ct);
+  s.nH = ceil_div(s.H, s.ch);
+  s.nW = ceil_div(s.W, s.cw);
+  s.V = s.ct * s.ch * s.cw;
+  if (s.ct > 1023 || s.ch > 1023 || s.cw > 1023) return VSA_ERR_UNSUPPORTED;
+  if (s.V > VSA_MAX_CUBE_VOLUME) return VSA_ERR_UNSUPPORTED;
+  s.nb = s.nT * s.nH * s.nW;
+  if (s.nb > VSA_MAX_BLOCKS) return VSA_ERR_UNSUPPORTED;
+  s.Pb = ceil_div(P, s.V);
+  s.N = P + s.T * s.H * s.W;
+  if (s.N > (int64_t)INT32_MAX / 2) return VSA_ERR_OVERFLOW;
+  return VSA_OK;
+}
+
+// A group of n values is either all zero (unset) or all >= 1.
+template <typename T>
+int group_state(const T* v, int n) {  // 0 unset, 1 set, -1 invalid
+  int zeros = 0, pos = 0;
+  for (int i = 0; i < n; ++i) {
+    zeros += v[i] == 0;
+    pos += v[i] >= 1;
+  }
+  return zeros == n ? 0 : pos == n ? 1 : -1;
+}
+
+// Row offsets of a [B][Hh][N][D] view: within a head in 32 bits, overall in
+// 64 bits, and 16-byte aligned.
+int check_view(int64_t B, int64_t Hh, int64_t N, int64_t D, int64_t sb, int64_t sh, int64_t sn) {
+  if ((N - 1) * sn + D > (int64_t)INT32_MAX) return VSA_ERR_OVERFLOW;
+  if (!span_fits(B, Hh, N, D, sb, sh, sn)) return VSA_ERR_OVERFLOW;
+  if (!aligned16_elems(sb) || !aligned16_elems(sh) || !aligned16_elems(sn)) return VSA_ERR_ALIGN;
+  return VSA_OK;
+}
+
 }  // namespace
 
 extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   if (pr == nullptr || out == nullptr) return VSA_ERR_INVALID_ARG;
-  const vsa_problem& p = *pr;
+  vsa_problem p = *pr;
   if (p.batch < 1 || p.heads < 1 || p.head_dim < 1 || p.prefix_len < 0) return VSA_ERR_INVALID_ARG;
   for (int a = 0; a < 3; ++a)
     if (p.latent[a] < 1 || p.cube[a] < 1) return VSA_ERR_INVALID_ARG;
   if (p.stride_b < 1 || p.stride_h < 1 || p.stride_n < 1 || p.o_stride_b < 1 ||
       p.o_stride_h < 1 || p.o_stride_n < 1)
     return VSA_ERR_INVALID_ARG;
+  // key side: unset groups take q's values
+  const int64_t kvs[3] = {p.kv_stride_b, p.kv_stride_h, p.kv_stride_n};
+  const int gl = group_state(p.latent_k, 3), gc = group_state(p.cube_k, 3), gs = group_state(kvs, 3);
+  if (gl < 0 || gc < 0 || gs < 0) return VSA_ERR_INVALID_ARG;
+  if (gl == 0) std::memcpy(p.latent_k, p.latent, sizeof(p.latent));
+  if (gc == 0) std::memcpy(p.cube_k, p.cube, sizeof(p.cube));
+  if (gs == 0) {
+    p.kv_stride_b = p.stride_b;
+    p.kv_stride_h = p.stride_h;
+    p.kv_stride_n = p.stride_n;
+  }
   if (p.dtype != VSA_DTYPE_BF16 && p.dtype != VSA_DTYPE_F16) return VSA_ERR_UNSUPPORTED;
   if (p.head_dim != 64 && p.head_dim != 128) return VSA_ERR_UNSUPPORTED;
 
-  const int64_t T = p.latent[0], H = p.latent[1], W = p.latent[2];
-  const int64_t ct = p.cube[0], ch = p.cube[1], cw = p.cube[2];
-  const int64_t nT = ceil_div(T, ct), nH = ceil_div(H, ch), nW = ceil_div(W, cw);
-  const int64_t V = ct * ch * cw;
-  if (V > VSA_MAX_CUBE_VOLUME) return VSA_ERR_UNSUPPORTED;
-  const int64_t nb = nT * nH * nW;
-  if (nb > VSA_MAX_BLOCKS) return VSA_ERR_UNSUPPORTED;
-  if (ct > 1023 || ch > 1023 || cw > 1023) return VSA_ERR_UNSUPPORTED;
   const int64_t P = p.prefix_len;
-  const int64_t Pb = ceil_div(P, V);
-  const int64_t nq = Pb + nb;
-  const int64_t N = P + T * H * W;
-  if (N > (int64_t)INT32_MAX / 2) return VSA_ERR_OVERFLOW;
+  Side q, k;
+  int st = derive_side(p.latent, p.cube, P, q);
+  if (st != VSA_OK) return st;
+  if ((st = derive_side(p.latent_k, p.cube_k, P, k)) != VSA_OK) return st;
+  const int64_t nq = q.Pb + q.nb;
+  const int64_t nb = k.nb;
   if (p.topk < 1 || p.topk > nb) return VSA_ERR_TOPK;
 
   // q/k/v/o rows: the kernels keep a row's element offset inside one head in
   // 32 bits; the (b, h) base offset is 64-bit.
   const int64_t D = p.head_dim;
-  if ((N - 1) * p.stride_n + D > (int64_t)INT32_MAX) return VSA_ERR_OVERFLOW;
-  if ((N - 1) * p.o_stride_n + D > (int64_t)INT32_MAX) return VSA_ERR_OVERFLOW;
-  if (!span_fits(p.batch, p.heads, N, D, p.stride_b, p.stride_h, p.stride_n) ||
-      !span_fits(p.batch, p.heads, N, D, p.o_stride_b, p.o_stride_h, p.o_stride_n))
-    return VSA_ERR_OVERFLOW;
-  if (!aligned16_elems(p.stride_b) || !aligned16_elems(p.stride_h) || !aligned16_elems(p.stride_n) ||
-      !aligned16_elems(p.o_stride_b) || !aligned16_elems(p.o_stride_h) ||
-      !aligned16_elems(p.o_stride_n))
-    return VSA_ERR_ALIGN;
+  const int64_t B = p.batch, Hh = p.heads;
+  if ((st = check_view(B, Hh, q.N, D, p.stride_b, p.stride_h, p.stride_n)) != VSA_OK) return st;
+  if ((st = check_view(B, Hh, q.N, D, p.o_stride_b, p.o_stride_h, p.o_stride_n)) != VSA_OK) return st;
+  if ((st = check_view(B, Hh, k.N, D, p.kv_stride_b, p.kv_stride_h, p.kv_stride_n)) != VSA_OK) return st;
   // output rows must not overlap (each token row is written by one lane pair)
   if (p.o_stride_n < D) return VSA_ERR_INVALID_ARG;
 
-  const int64_t BH = (int64_t)p.batch * p.heads;
+  const int64_t BH = B * Hh;
   const int64_t sel_elems = BH * nq * p.topk;
   if (sel_elems > (int64_t)INT32_MAX) return VSA_ERR_OVERFLOW;
 
   vsa_plan_t r;
   std::memset(&r, 0, sizeof(r));
   r.p = p;
-  r.nblk[0] = (int32_t)nT;
-  r.nblk[1] = (int32_t)nH;
-  r.nblk[2] = (int32_t)nW;
+  r.nblk[0] = (int32_t)q.nT;
+  r.nblk[1] = (int32_t)q.nH;
+  r.nblk[2] = (int32_t)q.nW;
   r.num_blocks = (int32_t)nb;
-  r.num_prefix_blocks = (int32_t)Pb;
+  r.num_prefix_blocks = (int32_t)q.Pb;
   r.num_q_blocks = (int32_t)nq;
-  r.cube_volume = (int32_t)V;
-  r.seq_len = N;
+  r.cube_volume = (int32_t)q.V;
+  r.seq_len = q.N;
+  r.nblk_k[0] = (int32_t)k.nT;
+  r.nblk_k[1] = (int32_t)k.nH;
+  r.nblk_k[2] = (int32_t)k.nW;
+  r.num_prefix_blocks_k = (int32_t)k.Pb;
+  r.cube_volume_k = (int32_t)k.V;
+  r.seq_len_k = k.N;
   const int64_t qbar_bytes = BH * nq * D * 4;
   r.kbar_offset = ceil_div(qbar_bytes, 256) * 256;
   r.workspace_bytes = r.kbar_offset + BH * nb * D * 4;
@@ -111,18 +167,27 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   }
   r.select_rows = rows;
 
-  // Attention tiling: query rows per workgroup by cube volume.
-  if (V <= 64) {
+  // Attention tiling: query rows per workgroup by the query cube volume.
+  if (q.V <= 64) {
     r.attend_variant = VSA_ATTEND_ROWS64;
     r.attend_tiles = 1;
   } else {
     r.attend_variant = VSA_ATTEND_ROWS256;
-    r.attend_tiles = (int32_t)ceil_div(V, 256);
+    r.attend_tiles = (int32_t)ceil_div(q.V, 256);
   }
   const int64_t grid = BH * nq * r.attend_tiles;
   if (grid > (int64_t)INT32_MAX) return VSA_ERR_OVERFLOW;
   *out = r;
   return VSA_OK;
+}
+
+extern "C" int vsa_topk_for_sparsity(int32_t num_blocks, double sparsity) {
+  if (num_blocks < 1 || !(sparsity >= 0.0 && sparsity < 1.0)) return VSA_ERR_INVALID_ARG;
+  // the 1e-9 absorbs the rounding of 1 - s (e.g. 120 * (1 - 0.9))
+  const double keep = std::floor((double)num_blocks * (1.0 - sparsity) + 0.5 + 1e-9);
+  if (keep < 1.0) return 1;
+  if (keep > (double)num_blocks) return num_blocks;
+  return (int)keep;
 }
 
 extern "C" int vsa_describe(const vsa_plan_t* plan, char* buf, size_t len) {
@@ -136,6 +201,16 @@ extern "C" int vsa_describe(const vsa_plan_t* plan, char* buf, size_t len) {
                         (long long)plan->seq_len, p.latent[0], p.latent[1], p.latent[2], p.cube[0],
                         p.cube[1], p.cube[2], plan->num_blocks, p.topk, keep);
   if (n < 0) return VSA_ERR_INVALID_ARG;
+  const bool own_k = std::memcmp(p.latent_k, p.latent, sizeof(p.latent)) != 0 ||
+                     std::memcmp(p.cube_k, p.cube, sizeof(p.cube)) != 0;
+  if (own_k) {  // key side of a two-grid problem
+    const int m = std::snprintf(tmp + n, sizeof(tmp) - (size_t)n,
+                                ", kv_seq_len=%lld, kv_seq_shape=(%d, %d, %d), kv_block_size=(%d, %d, %d)",
+                                (long long)plan->seq_len_k, p.latent_k[0], p.latent_k[1], p.latent_k[2],
+                                p.cube_k[0], p.cube_k[1], p.cube_k[2]);
+    if (m < 0) return VSA_ERR_INVALID_ARG;
+    n += m;
+  }
   if (len > 0) {
     size_t c = (size_t)n < len - 1 ? (size_t)n : len - 1;
     std::memcpy(buf, tmp, c);

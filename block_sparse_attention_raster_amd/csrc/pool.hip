@@ -1,7 +1,8 @@
 // Block mean-pool (the "mean" of q and k per block that the block scores use;
 // "FastVideo VSA" user guide, opening definition: every query block scores
 // the key/value blocks). One workgroup pools one block of one (batch, head):
-// q for every query block (prefix blocks and cubes), k for every cube. Only
+// q for every query block (prefix blocks and cubes) of q's grid, k for every
+// cube of k's grid. Only
 // the block's valid tokens are read and the sum is divided by their count.
 // Reads go through the in-kernel index map, 16 bytes per lane; the sum is
 // float32 and the result float32. Inputs are bf16 or fp16.
@@ -26,12 +27,14 @@ __global__ __launch_bounds__(kPoolThreads) void vsa_pool_kernel(VsaArgs a, const
   const int task = blockIdx.x - bh * per_head;
   const int b = bh / a.Hh, h = bh - b * a.Hh;
   const bool isq = task < a.nq;
-  const int blk = isq ? task : a.Pb + (task - a.nq);
-  const __bf16* src = (isq ? q : k) + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const VsaGrid& g = isq ? a.gq : a.gk;
+  const int blk = isq ? task : a.gk.Pb + (task - a.nq);
+  const __bf16* src = isq ? q + (int64_t)b * a.sb + (int64_t)h * a.sh : k + (int64_t)b * a.ksb + (int64_t)h * a.ksh;
+  const int32_t sn = isq ? a.sn : a.ksn;
   float* dst = isq ? qbar + ((int64_t)bh * a.nq + task) * D
                    : kbar + ((int64_t)bh * a.nb + (task - a.nq)) * D;
 
-  const BlockExt e = block_ext(a, blk);
+  const BlockExt e = block_ext(g, blk);
   const int c = threadIdx.x % CPR;
   const int rsub = threadIdx.x / CPR;
 
@@ -41,8 +44,8 @@ __global__ __launch_bounds__(kPoolThreads) void vsa_pool_kernel(VsaArgs a, const
 
 #pragma unroll 4
   for (int r = rsub; r < e.n; r += RPP) {
-    const int row = slot_row(a, e, r);
-    const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)row * a.sn + c * 8);
+    const int row = slot_row(g, e, r);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)row * sn + c * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (F16) {   // fp16 inputs (exact in float)

@@ -21,29 +21,41 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Everything the kernels need, passed by value.
-struct VsaArgs {
-  int32_t B, Hh, D;
+// One side's grid and its cutting into blocks: q's (query blocks) or
+// k/v's (key blocks). The two differ when q and k/v lie on different
+// latent grids or use different cube shapes (fastbsa package page, section
+// "Use": separate latent and chunk shapes for q and k).
+struct VsaGrid {
   int32_t T, H, W;
   int32_t ct, ch, cw;
   int32_t nT, nH, nW;
-  int32_t P, V, Pb, nb, nq;
-  int32_t topk;
-  int64_t sb, sh;  // q/k/v batch and head strides (elements)
-  int32_t sn;      // q/k/v token stride (elements)
-  int64_t osb, osh;
-  int32_t osn;
-  float scale_log2e;     // head_dim^-1/2 * log2(e)
-  int32_t select_rows;   // query blocks per score/top-k workgroup
-  int32_t tiles;         // query row tiles per query block
+  int32_t P, V, Pb, nb;  // prefix tokens, cube volume, prefix blocks, cubes
   uint64_t magic_nW;     // ceil(2^32 / nW): floor(x / nW) = (x * magic) >> 32 for x < 2^16
   uint64_t magic_nH;     // ceil(2^32 / nH)
-  int32_t f16;           // q, k, v, o are fp16 (else bf16)
   // Division magics of the valid extents of cubes: ew in {cw, W - (nW-1)*cw}
   // (index 0: whole, 1: tail) and eh*ew with index 2*[eh is the tail] +
   // [ew is the tail].
   uint64_t magic_ew[2];
   uint64_t magic_ehw[4];
+};
+
+// Everything the kernels need, passed by value.
+struct VsaArgs {
+  int32_t B, Hh, D;
+  VsaGrid gq, gk;        // query side, key/value side
+  int32_t nq;            // query blocks: gq.Pb + gq.nb
+  int32_t nb;            // key cubes: gk.nb (the ids sel holds)
+  int32_t topk;
+  int64_t sb, sh;        // q batch and head strides (elements)
+  int32_t sn;            // q token stride (elements)
+  int64_t ksb, ksh;      // k and v strides
+  int32_t ksn;
+  int64_t osb, osh;
+  int32_t osn;
+  float scale_log2e;     // head_dim^-1/2 * log2(e)
+  int32_t select_rows;   // query blocks per score/top-k workgroup
+  int32_t tiles;         // query row tiles per query block
+  int32_t f16;           // q, k, v, o are fp16 (else bf16)
 };
 
 // Valid region of one block: first token row, extents of the (tt, hh, ww)
@@ -54,39 +66,39 @@ struct BlockExt {
   int32_t n;
 };
 
-__device__ __forceinline__ BlockExt block_ext(const VsaArgs& a, int32_t blk) {
+__device__ __forceinline__ BlockExt block_ext(const VsaGrid& g, int32_t blk) {
   BlockExt e;
-  if (blk < a.Pb) {
-    const int32_t s = blk * a.V;
-    const int32_t n = min(a.V, a.P - s);
+  if (blk < g.Pb) {
+    const int32_t s = blk * g.V;
+    const int32_t n = min(g.V, g.P - s);
     e.base = s;
     e.eh = 1;
     e.ew = n;
     e.n = n;
     return e;
   }
-  const int32_t c = blk - a.Pb;
-  const int32_t bw = c % a.nW;
-  const int32_t rest = c / a.nW;
-  const int32_t bh = rest % a.nH;
-  const int32_t bt = rest / a.nH;
-  const int32_t t0 = bt * a.ct, h0 = bh * a.ch, w0 = bw * a.cw;
-  const int32_t et = min(a.ct, a.T - t0);
-  e.eh = min(a.ch, a.H - h0);
-  e.ew = min(a.cw, a.W - w0);
-  e.base = a.P + (t0 * a.H + h0) * a.W + w0;
+  const int32_t c = blk - g.Pb;
+  const int32_t bw = c % g.nW;
+  const int32_t rest = c / g.nW;
+  const int32_t bh = rest % g.nH;
+  const int32_t bt = rest / g.nH;
+  const int32_t t0 = bt * g.ct, h0 = bh * g.ch, w0 = bw * g.cw;
+  const int32_t et = min(g.ct, g.T - t0);
+  e.eh = min(g.ch, g.H - h0);
+  e.ew = min(g.cw, g.W - w0);
+  e.base = g.P + (t0 * g.H + h0) * g.W + w0;
   e.n = et * e.eh * e.ew;
   return e;
 }
 
 // Token row of compact slot r (0 <= r < e.n) of a block.
-__device__ __forceinline__ int32_t slot_row(const VsaArgs& a, const BlockExt& e, int32_t r) {
+__device__ __forceinline__ int32_t slot_row(const VsaGrid& g, const BlockExt& e, int32_t r) {
   const uint32_t ehw = (uint32_t)(e.eh * e.ew);
   const uint32_t tt = (uint32_t)r / ehw;
   const uint32_t rem = (uint32_t)r - tt * ehw;
   const uint32_t hh = rem / (uint32_t)e.ew;
   const uint32_t ww = rem - hh * (uint32_t)e.ew;
-  return e.base + ((int32_t)tt * a.H + (int32_t)hh) * a.W + (int32_t)ww;
+  return e.base + ((int32_t)tt * g.H + (int32_t)hh) * g.W + (int32_t)ww;
 }
 
 __device__ __forceinline__ uint32_t orderable_key(float f) {

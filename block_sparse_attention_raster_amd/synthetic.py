@@ -136,6 +136,21 @@ def make_inputs(w: Workload, seed: Optional[int] = None, dtype: str = "bf16"):
     return conv(q), conv(k), conv(v)
 
 
+def make_inputs_two_grids(seed: int, batch: int, heads: int, head_dim: int, seq_len_q: int,
+                          seq_len_k: int, dtype: str = "bf16"):
+    """(q, k, v) for q and k/v on different grids: q [B, Hh, Nq, D] then k
+    and v [B, Hh, Nk, D], drawn in that order with the recipe above (no
+    modification)."""
+    if dtype not in ("bf16", "f16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((batch, heads, seq_len_q, head_dim), dtype=np.float32)
+    k = rng.standard_normal((batch, heads, seq_len_k, head_dim), dtype=np.float32)
+    v = rng.standard_normal((batch, heads, seq_len_k, head_dim), dtype=np.float32)
+    conv = f32_to_bf16_bits if dtype == "bf16" else f32_to_f16_bits
+    return conv(q), conv(k), conv(v)
+
+
 def _modify(w: Workload, rng, k: np.ndarray) -> None:
     if w.modification == "none":
         return

@@ -24,9 +24,11 @@
  *                "Verify routing and fallback": the Wan route takes FP16
  *                or BF16), element (b, h, n, d) at
  *                b*stride_b + h*stride_h + n*stride_n + d   (elements);
- *                d is contiguous. q, k and v share one set of strides; o has
- *                its own. Base pointers and strides*2 must be multiples of
- *                16 bytes.
+ *                d is contiguous. q, k and v share one set of strides
+ *                unless kv_stride_* are given; o has its own. Base pointers
+ *                and strides*2 must be multiples of 16 bytes. With a key
+ *                grid of its own, k and v hold N_k = P + T_k*H_k*W_k rows
+ *                in raster order of that grid.
  *   workspace    float32 pooled means, written by vsa_select:
  *                  qbar [B][Hh][num_q_blocks][head_dim], then
  *                  kbar [B][Hh][num_blocks][head_dim] at byte offset
@@ -90,19 +92,31 @@ typedef struct vsa_problem {
   int32_t topk;           /* cubes kept per query block, 1..num_blocks       */
   int32_t prefix_len;     /* P >= 0 tokens before the grid, always kept      */
   int32_t dtype;          /* VSA_DTYPE_BF16 or VSA_DTYPE_F16                 */
-  int64_t stride_b, stride_h, stride_n;        /* q, k, v strides (elements) */
+  int64_t stride_b, stride_h, stride_n;        /* q strides (elements); k and
+                                                  v too unless kv_stride_* set */
   int64_t o_stride_b, o_stride_h, o_stride_n;  /* o strides (elements)       */
+  /* k and v on a grid of their own (fastbsa package page, section "Use":
+     latent_shape_k and chunk_3d_shape_k next to q's shapes). Each group
+     all zero means "same as q". Query blocks then come from (latent, cube),
+     key blocks from (latent_k, cube_k); prefix_len counts leading tokens of
+     both sequences, each side cutting its prefix by its own cube volume. */
+  int32_t latent_k[3];    /* (T, H, W) of k and v, each >= 1, or all 0      */
+  int32_t cube_k[3];      /* key cube shape, each >= 1, or all 0            */
+  int64_t kv_stride_b, kv_stride_h, kv_stride_n;  /* k, v strides, or all 0 */
 } vsa_problem;
 
-/* Derived geometry; filled by vsa_plan, plain data, owned by the caller. */
+/* Derived geometry; filled by vsa_plan, plain data, owned by the caller.
+   p holds the problem with the key-side groups filled in (never zero). */
 typedef struct vsa_plan_t {
   vsa_problem p;
-  int32_t nblk[3];            /* cubes per axis: ceil(T/ct), ceil(H/ch), ceil(W/cw) */
-  int32_t num_blocks;         /* video cubes nT*nH*nW                        */
-  int32_t num_prefix_blocks;  /* ceil(P / V)                                 */
-  int32_t num_q_blocks;       /* num_prefix_blocks + num_blocks              */
+  int32_t nblk[3];            /* query cubes per axis: ceil(T/ct), ceil(H/ch), ceil(W/cw) */
+  int32_t num_blocks;         /* key cubes nT_k*nH_k*nW_k: the ids sel holds
+                                 (equal to the query cube count when k and v
+                                 share q's grid and cube)                   */
+  int32_t num_prefix_blocks;  /* query prefix blocks ceil(P / V)             */
+  int32_t num_q_blocks;       /* num_prefix_blocks + query cubes             */
   int32_t cube_volume;        /* V = ct*ch*cw                                */
-  int64_t seq_len;            /* N = P + T*H*W                               */
+  int64_t seq_len;            /* N = P + T*H*W tokens of q and o             */
   int64_t workspace_bytes;    /* bytes of float32 workspace vsa_select needs */
   int64_t kbar_offset;        /* byte offset of kbar inside the workspace    */
   int64_t sel_elems;          /* B*Hh*num_q_blocks*topk                      */
@@ -110,6 +124,10 @@ typedef struct vsa_plan_t {
   int32_t select_rows;        /* query blocks per score/top-k workgroup      */
   int32_t attend_variant;     /* attention kernel tiling chosen by the plan  */
   int32_t attend_tiles;       /* query row tiles per query block             */
+  int32_t nblk_k[3];          /* key cubes per axis                          */
+  int32_t num_prefix_blocks_k;/* key prefix blocks ceil(P / V_k), all kept   */
+  int32_t cube_volume_k;      /* V_k                                         */
+  int64_t seq_len_k;          /* N_k = P + T_k*H_k*W_k tokens of k and v     */
 } vsa_plan_t;
 
 /* Validate a problem and derive its geometry. Host only: no device work,
@@ -117,6 +135,13 @@ typedef struct vsa_plan_t {
  * *out unspecified. The Wan routing-log shape (31, 22, 40) with (4, 8, 8)
  * cubes gives num_blocks = 120 (user guide, "Wan top-k behavior"). */
 int vsa_plan(const vsa_problem* problem, vsa_plan_t* out);
+
+/* Top-k for a sparsity s in [0, 1), the fraction of key cubes dropped
+ * (fastbsa package page, section "Use": sparsity=0.9375 keeps 1/16): the
+ * nearest integer to num_blocks * (1 - s), halves rounded up, clamped to
+ * 1..num_blocks. Returns it, or VSA_ERR_INVALID_ARG for num_blocks < 1 or
+ * s outside [0, 1) (NaN included). Host only. */
+int vsa_topk_for_sparsity(int32_t num_blocks, double sparsity);
 
 /* Block selection (pages: user guide opening definition; fastbsa "How it
  * works": the score matrix never leaves on-chip memory). Pools q over every

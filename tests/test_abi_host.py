@@ -175,3 +175,68 @@ def test_status_strings():
     for s in range(-7, 1):
         assert _lib.status_str(s) not in ("", "unknown status")
     assert _lib.status_str(-99) == "unknown status"
+
+
+# ---------------------------------------------------------------------------
+# q and k/v on different grids; sparsity -> top-k (fastbsa package page,
+# section "Use")
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lq,cq,lk,ck,prefix", [
+    ((8, 30, 52), (4, 4, 4), (16, 30, 52), (4, 4, 4), 0),
+    ((4, 6, 5), (2, 2, 3), (3, 5, 7), (2, 4, 4), 0),
+    ((2, 4, 4), (1, 2, 2), (4, 4, 4), (2, 2, 2), 6),
+    ((31, 22, 40), (4, 8, 8), (31, 22, 40), (4, 4, 4), 64),
+])
+def test_plan_two_grids_match_oracle(lq, cq, lk, ck, prefix):
+    pl = vsa.plan(2, 3, 128, lq, cq, 1, prefix, latent_k=lk, cube_k=ck)
+    gq, gk = O.geometry(lq, cq, prefix), O.geometry(lk, ck, prefix)
+    assert (pl.num_prefix_blocks, pl.num_q_blocks, pl.seq_len, pl.cube_volume) == \
+        (gq.num_prefix_blocks, gq.num_q_blocks, gq.seq_len, gq.cube_volume)
+    assert (pl.num_blocks, pl.num_prefix_blocks_k, pl.seq_len_k, pl.cube_volume_k, pl.nblk_k) == \
+        (gk.num_blocks, gk.num_prefix_blocks, gk.seq_len, gk.cube_volume, gk.nblk)
+    assert np.array_equal(pl.valid_counts("q"), gq.counts)
+    assert np.array_equal(pl.valid_counts("k"), gk.counts)
+    Nk = gk.seq_len
+    assert pl.kv_strides == (3 * Nk * 128, Nk * 128, 128)
+    assert pl.workspace_bytes == pl.kbar_offset + 2 * 3 * gk.num_blocks * 128 * 4
+    assert pl.kbar_offset >= 2 * 3 * gq.num_q_blocks * 128 * 4
+    assert pl.sel_elems == 2 * 3 * gq.num_q_blocks
+    d = vsa.describe(pl)
+    assert ("kv_seq_shape" in d) == ((lq, cq) != (lk, ck))
+
+
+def test_plan_two_grids_status_codes():
+    base = dict(batch=1, heads=2, head_dim=128, latent=(8, 8, 8), cube=(4, 4, 4), topk=4)
+    # top-k is bounded by the key cube count, not the query cube count
+    assert _status(**base, latent_k=(8, 8, 4)) == _lib.VSA_OK
+    assert _status(**dict(base, topk=5), latent_k=(8, 8, 4)) == _lib.VSA_ERR_TOPK
+    assert _status(**base, cube_k=(8, 16, 16)) == _lib.VSA_ERR_UNSUPPORTED
+    assert _status(**base, latent_k=(8, 8, 8), kv_strides=(64 * 512, 64 * 128, 60)) == _lib.VSA_ERR_ALIGN
+    pl = vsa.plan(**base)
+    out = _lib.VsaPlan()
+    for field, val in (("latent_k", (0, 8, 8)), ("cube_k", (4, 0, 0))):
+        pr = _lib.VsaProblem.from_buffer_copy(pl.raw.p)
+        getattr(pr, field)[:] = list(val)
+        assert _lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(out)) == _lib.VSA_ERR_INVALID_ARG
+    pr = _lib.VsaProblem.from_buffer_copy(pl.raw.p)
+    pr.kv_stride_b, pr.kv_stride_h, pr.kv_stride_n = 0, 0, 128
+    assert _lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(out)) == _lib.VSA_ERR_INVALID_ARG
+    # all-zero key groups take q's values, and the plan holds them filled in
+    pr = _lib.VsaProblem.from_buffer_copy(pl.raw.p)
+    pr.latent_k[:], pr.cube_k[:] = [0, 0, 0], [0, 0, 0]
+    pr.kv_stride_b = pr.kv_stride_h = pr.kv_stride_n = 0
+    assert _lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(out)) == _lib.VSA_OK
+    assert tuple(out.p.latent_k) == (8, 8, 8) and tuple(out.p.cube_k) == (4, 4, 4)
+    assert (out.p.kv_stride_b, out.p.kv_stride_h, out.p.kv_stride_n) == \
+        (out.p.stride_b, out.p.stride_h, out.p.stride_n)
+    assert out.num_blocks == pl.num_blocks and out.seq_len_k == out.seq_len
+
+
+def test_topk_for_sparsity_matches_oracle():
+    for nb in (1, 2, 7, 8, 120, 624, 960, 4096, 16384):
+        for s in (0.0, 0.25, 0.5, 0.75, 0.8, 0.9, 0.9375, 0.95, 0.99, 0.999999):
+            assert vsa.topk_for_sparsity(nb, s) == O.topk_for_sparsity(nb, s), (nb, s)
+    L = _lib.lib()
+    for nb, s in ((120, 1.0), (120, -0.01), (120, float("nan")), (0, 0.5), (-3, 0.5)):
+        assert L.vsa_topk_for_sparsity(nb, s) == _lib.VSA_ERR_INVALID_ARG

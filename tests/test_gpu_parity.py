@@ -284,3 +284,95 @@ def test_workload_prefix():
 def test_workload_prefix_f16():
     w = synthetic.WORKLOADS["prefix"]
     _full_check(w, 96, heads=[(0, 0), (1, 23)], blocks_per_head=12, dtype="f16")
+
+
+# ---------------------------------------------------------------------------
+# q and k/v on different grids (fastbsa package page, section "Use")
+# ---------------------------------------------------------------------------
+
+CROSS = [
+    # name, B, Hh, D, latent_q, cube_q, latent_k, cube_k, topk, prefix
+    ("cross_longer_kv", 1, 2, 128, (4, 10, 12), (4, 4, 4), (8, 10, 12), (4, 4, 4), 6, 0),
+    ("cross_q256_k64", 1, 2, 128, (9, 10, 11), (4, 8, 8), (9, 10, 11), (4, 4, 4), 8, 0),
+    ("cross_q64_k256", 1, 2, 128, (6, 8, 10), (4, 4, 4), (5, 9, 17), (4, 8, 8), 3, 0),
+    ("cross_prefix", 2, 2, 64, (3, 6, 7), (2, 4, 4), (5, 5, 9), (4, 4, 4), 4, 40),
+    ("cross_odd_shapes", 1, 2, 128, (5, 7, 9), (3, 4, 5), (6, 5, 8), (2, 3, 3), 5, 9),
+    ("cross_q256_kprefix", 1, 2, 128, (5, 9, 17), (4, 8, 8), (7, 6, 9), (2, 4, 4), 4, 100),
+]
+
+
+def _cross_check(name, B, Hh, D, lq, cq, lk, ck, topk, P, dtype="bf16", heads=None, blocks_per_head=None,
+                 use_sparsity=None):
+    import torch
+    import block_sparse_attention_raster_amd as vsa
+    gq, gk = O.geometry(lq, cq, P), O.geometry(lk, ck, P)
+    _announce(f"{name}: B={B} Hh={Hh} D={D} q={lq}/{cq} k={lk}/{ck} P={P} topk={topk} dtype={dtype}")
+    bits = synthetic.make_inputs_two_grids(zlib.crc32(name.encode()) & 0xFFFF, B, Hh, D, gq.seq_len,
+                                           gk.seq_len, dtype)
+    q, k, v = (G.to_device(x, dtype) for x in bits)
+    if use_sparsity is None:
+        pl = vsa.plan_for(q, lq, cq, topk, P, k=k, latent_k=lk, cube_k=ck)
+        sel, ws = vsa.select(pl, q, k)
+        out = vsa.attend(pl, q, k, v, sel)
+    else:
+        assert P == 0
+        out = vsa.flash_attn_bsa_3d(q, k, v, lq, lk, sparsity=use_sparsity, chunk_3d_shape_q=cq,
+                                    chunk_3d_shape_k=ck)
+        pl = vsa.plan_for(q, lq, cq, topk, P, k=k, latent_k=lk, cube_k=ck)
+        sel, ws = vsa.select(pl, q, k)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy().astype(np.int64)
+    got = G.from_device(out, dtype)
+    qf_all, kf_all = O.decode(bits[0], dtype), O.decode(bits[1], dtype)
+    scores = O.block_scores(O.pool(qf_all, gq), O.pool(kf_all, gk, video_only=True), D)
+    chk = O.check_selection(sel, scores, topk, band=G.TIE_BAND)
+    assert chk["mismatch_rows"] == [], chk["mismatch_rows"][:10]
+    worst = {"max_abs": 0.0, "rel_l2": 0.0}
+    rng = np.random.default_rng(0)
+    for (b, h) in (heads or [(b, h) for b in range(B) for h in range(Hh)]):
+        qf, kf, vf = (O.decode(x[b, h], dtype) for x in bits)
+        blocks = range(gq.num_q_blocks) if blocks_per_head is None else sorted(
+            set(rng.choice(gq.num_q_blocks, size=blocks_per_head, replace=False).tolist())
+            | {0, gq.num_q_blocks - 1})
+        blocks = list(blocks)
+        ref = O.attend_dense_masked(qf, kf, vf, sel[b, h], gq, query_blocks=blocks, gk=gk)
+        rows = np.concatenate([gq.members[i] for i in blocks])
+        assert np.all(np.isfinite(got[b, h][rows]))
+        e = O.error_norms(got[b, h][rows], ref[rows])
+        worst = {key: max(worst[key], e[key]) for key in worst}
+    _announce(f"{name}/{dtype}: band rows {chk['band_rows']} of {chk['rows']}, "
+              f"max_abs {worst['max_abs']:.3e} rel_l2 {worst['rel_l2']:.3e}")
+    assert worst["max_abs"] <= G.TOL[dtype]["max_abs"] and worst["rel_l2"] <= G.TOL[dtype]["rel_l2"], worst
+
+
+@pytest.mark.parametrize("case", CROSS, ids=[c[0] for c in CROSS])
+def test_two_grids_full_oracle(case):
+    _cross_check(*case)
+
+
+def test_two_grids_f16():
+    _cross_check(*CROSS[1], dtype="f16")
+
+
+def test_two_grids_sparsity_front_end():
+    """fastbsa's call with sparsity 0.9375 (package page, section "Use"): q
+    on an (8, 30, 52) grid, k and v on (16, 30, 52), (4, 4, 4) chunks: 416
+    key chunks, 26 kept."""
+    import block_sparse_attention_raster_amd as vsa
+    assert vsa.topk_for_sparsity(416, 0.9375) == 26
+    _cross_check("cross_sparsity", 1, 4, 128, (8, 30, 52), (4, 4, 4), (16, 30, 52), (4, 4, 4), 26, 0,
+                 heads=[(0, 0), (0, 3)], blocks_per_head=12, use_sparsity=0.9375)
+
+
+def test_two_grids_api_with_equal_grids_is_bitwise_the_same():
+    """Giving k's grid explicitly, equal to q's, changes nothing."""
+    import torch
+    import block_sparse_attention_raster_amd as vsa
+    w = synthetic.custom_workload("same_grid", seed=31, batch=1, heads=2, head_dim=128,
+                                  latent=(5, 9, 17), cube=(4, 8, 8), topk=3, prefix_len=20)
+    q, k, v = (G.to_device(x) for x in synthetic.make_inputs(w))
+    a, sa = vsa.forward(q, k, v, w.latent, w.cube, 3, 20, return_sel=True)
+    b, sb = vsa.forward(q, k, v, w.latent, w.cube, 3, 20, return_sel=True, latent_shape_k=w.latent,
+                        cube_shape_k=w.cube)
+    torch.cuda.synchronize()
+    assert torch.equal(sa, sb) and torch.equal(a, b)
