@@ -23,8 +23,8 @@ from typing import Optional, Sequence, Tuple
 from . import _lib
 from ._lib import VsaError
 
-__all__ = ["Plan", "VsaError", "plan", "plan_for", "select", "attend", "forward", "flash_attn_bsa_3d",
-           "topk_for_sparsity", "describe"]
+__all__ = ["Plan", "Route", "VsaError", "plan", "plan_for", "select", "attend", "forward",
+           "flash_attn_bsa_3d", "topk_for_sparsity", "route", "describe"]
 
 
 class Plan:
@@ -84,6 +84,15 @@ def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Seq
     ``dtype`` is "bf16" or "f16", the element type of q, k, v and o.
     ``latent_k`` and ``cube_k`` put k and v on a grid of their own (default:
     q's); ``kv_strides`` then default to a contiguous layout of that grid."""
+    raw = _lib.VsaPlan()
+    pr = _problem(batch, heads, head_dim, latent, cube, topk, prefix_len, strides, o_strides, dtype,
+                  latent_k, cube_k, kv_strides)
+    _lib.check(_lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(raw)), "vsa_plan")
+    return Plan(raw)
+
+
+def _problem(batch, heads, head_dim, latent, cube, topk, prefix_len=0, strides=None, o_strides=None,
+             dtype="bf16", latent_k=None, cube_k=None, kv_strides=None) -> _lib.VsaProblem:
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be one of {sorted(_DTYPES)}, got {dtype!r}")
     N = int(prefix_len) + int(latent[0]) * int(latent[1]) * int(latent[2])
@@ -109,9 +118,7 @@ def plan(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Seq
     pr.latent_k[:] = [int(x) for x in latent_k]
     pr.cube_k[:] = [int(x) for x in cube_k]
     pr.kv_stride_b, pr.kv_stride_h, pr.kv_stride_n = (int(s) for s in kv_strides)
-    raw = _lib.VsaPlan()
-    _lib.check(_lib.lib().vsa_plan(ctypes.byref(pr), ctypes.byref(raw)), "vsa_plan")
-    return Plan(raw)
+    return pr
 
 
 def _torch_dtype(pl: Plan):
@@ -245,6 +252,54 @@ def flash_attn_bsa_3d(q, k, v, latent_shape_q: Sequence[int], latent_shape_k: Se
         topk = topk_for_sparsity(nb_k, sparsity)
     return forward(q, k, v, latent_shape_q, chunk_3d_shape_q, topk, prefix_len, out,
                    latent_shape_k=latent_shape_k, cube_shape_k=chunk_3d_shape_k)
+
+
+_ROUTES = {_lib.VSA_ROUTE_VSA: "VSA", _lib.VSA_ROUTE_VSA_ALL_BLOCKS: "VSA_ALL_BLOCKS",
+           _lib.VSA_ROUTE_DENSE: "SDPA"}
+_MODES = {"native": _lib.VSA_CHECKPOINT_NATIVE, "dmd": _lib.VSA_CHECKPOINT_DMD}
+
+
+class Route:
+    """A routing decision (vsa_route): ``route`` is "VSA", "VSA_ALL_BLOCKS"
+    or "SDPA" (dense attention, which the caller runs; this library has no
+    dense path), ``reason`` a VSA_REASON_* code, ``plan`` the plan to run
+    the sparse kernels with (None on a dense route without geometry)."""
+
+    def __init__(self, raw: _lib.VsaRoute):
+        self.raw = raw
+        self.route = _ROUTES[raw.route]
+        self.reason = raw.reason
+        self.status = raw.status
+        self.topk = raw.topk
+        self.plan = Plan(_lib.VsaPlan.from_buffer_copy(raw.plan)) if raw.has_plan else None
+
+    @property
+    def sparse(self) -> bool:
+        return self.route != "SDPA"
+
+    def log_line(self) -> str:
+        buf = ctypes.create_string_buffer(768)
+        n = _lib.lib().vsa_describe_route(ctypes.byref(self.raw), buf, len(buf))
+        if n < 0:
+            raise VsaError(n, "vsa_describe_route")
+        return buf.value.decode()
+
+    def __repr__(self):
+        return f"Route({self.log_line()})"
+
+
+def route(batch: int, heads: int, head_dim: int, latent: Sequence[int], cube: Sequence[int], topk: int,
+          prefix_len: int = 0, checkpoint_mode: str = "native", **kw) -> Route:
+    """Routing decision for a problem (vsa_route; the user guide's Wan rules:
+    topk > num_blocks and, on a native checkpoint, topk == num_blocks go to
+    dense attention; a DMD checkpoint keeps every block on the sparse path).
+    ``kw`` are ``plan``'s optional arguments."""
+    if checkpoint_mode not in _MODES:
+        raise ValueError(f"checkpoint_mode must be one of {sorted(_MODES)}")
+    pr = _problem(batch, heads, head_dim, latent, cube, topk, prefix_len, **kw)
+    raw = _lib.VsaRoute()
+    _lib.check(_lib.lib().vsa_route(ctypes.byref(pr), _MODES[checkpoint_mode], ctypes.byref(raw)), "vsa_route")
+    return Route(raw)
 
 
 def describe(pl: Plan) -> str:

@@ -19,7 +19,17 @@ VSA_DTYPE_BF16 = 0
 VSA_DTYPE_F16 = 1
 
 EXPORTED = ("vsa_plan", "vsa_topk_for_sparsity", "vsa_select", "vsa_attend", "vsa_forward",
-            "vsa_describe", "vsa_status_str")
+            "vsa_describe", "vsa_status_str", "vsa_route", "vsa_describe_route")
+
+VSA_ROUTE_VSA = 0
+VSA_ROUTE_VSA_ALL_BLOCKS = 1
+VSA_ROUTE_DENSE = 2
+VSA_CHECKPOINT_NATIVE = 0
+VSA_CHECKPOINT_DMD = 1
+VSA_REASON_NONE = 0
+VSA_REASON_TOPK_ABOVE_BLOCKS = 1
+VSA_REASON_ALL_BLOCKS_NATIVE = 2
+VSA_REASON_UNSUPPORTED = 3
 
 
 class VsaProblem(ctypes.Structure):
@@ -47,6 +57,14 @@ class VsaPlan(ctypes.Structure):
         ("attend_tiles", ctypes.c_int32),
         ("nblk_k", ctypes.c_int32 * 3), ("num_prefix_blocks_k", ctypes.c_int32),
         ("cube_volume_k", ctypes.c_int32), ("seq_len_k", ctypes.c_int64),
+    ]
+
+
+class VsaRoute(ctypes.Structure):
+    _fields_ = [
+        ("route", ctypes.c_int32), ("reason", ctypes.c_int32), ("status", ctypes.c_int32),
+        ("checkpoint_mode", ctypes.c_int32), ("topk", ctypes.c_int32), ("has_plan", ctypes.c_int32),
+        ("plan", VsaPlan),
     ]
 
 
@@ -82,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.vsa_forward.restype = ctypes.c_int
         L.vsa_describe.argtypes = [ctypes.POINTER(VsaPlan), ctypes.c_char_p, ctypes.c_size_t]
         L.vsa_describe.restype = ctypes.c_int
+        L.vsa_route.argtypes = [ctypes.POINTER(VsaProblem), ctypes.c_int32, ctypes.POINTER(VsaRoute)]
+        L.vsa_route.restype = ctypes.c_int
+        L.vsa_describe_route.argtypes = [ctypes.POINTER(VsaRoute), ctypes.c_char_p, ctypes.c_size_t]
+        L.vsa_describe_route.restype = ctypes.c_int
         L.vsa_status_str.argtypes = [ctypes.c_int]
         L.vsa_status_str.restype = ctypes.c_char_p
         _lib = L

@@ -219,6 +219,94 @@ extern "C" int vsa_describe(const vsa_plan_t* plan, char* buf, size_t len) {
   return n;
 }
 
+extern "C" int vsa_route(const vsa_problem* pr, int32_t checkpoint_mode, vsa_route_t* out) {
+  if (pr == nullptr || out == nullptr) return VSA_ERR_INVALID_ARG;
+  if (checkpoint_mode != VSA_CHECKPOINT_NATIVE && checkpoint_mode != VSA_CHECKPOINT_DMD)
+    return VSA_ERR_INVALID_ARG;
+  if (pr->topk < 1) return VSA_ERR_TOPK;
+  vsa_route_t r;
+  std::memset(&r, 0, sizeof(r));
+  r.checkpoint_mode = checkpoint_mode;
+  r.topk = pr->topk;
+  vsa_problem p = *pr;
+  int st = vsa_plan(&p, &r.plan);
+  if (st == VSA_ERR_TOPK) {
+    // topk above the block count: plan with every block for the geometry
+    p.topk = 1;
+    if (vsa_plan(&p, &r.plan) == VSA_OK) {
+      p.topk = r.plan.num_blocks;
+      st = vsa_plan(&p, &r.plan);
+      r.has_plan = st == VSA_OK;
+      r.route = VSA_ROUTE_DENSE;
+      r.reason = VSA_REASON_TOPK_ABOVE_BLOCKS;
+      *out = r;
+      return VSA_OK;
+    }
+    st = vsa_plan(&p, &r.plan);   // the shape itself is refused
+  }
+  if (st != VSA_OK) {
+    std::memset(&r.plan, 0, sizeof(r.plan));
+    r.route = VSA_ROUTE_DENSE;
+    r.reason = VSA_REASON_UNSUPPORTED;
+    r.status = st;
+    *out = r;
+    return VSA_OK;
+  }
+  r.has_plan = 1;
+  if (pr->topk == r.plan.num_blocks) {
+    if (checkpoint_mode == VSA_CHECKPOINT_NATIVE) {
+      r.route = VSA_ROUTE_DENSE;
+      r.reason = VSA_REASON_ALL_BLOCKS_NATIVE;
+    } else {
+      r.route = VSA_ROUTE_VSA_ALL_BLOCKS;
+    }
+  } else {
+    r.route = VSA_ROUTE_VSA;
+  }
+  *out = r;
+  return VSA_OK;
+}
+
+extern "C" int vsa_describe_route(const vsa_route_t* r, char* buf, size_t len) {
+  if (r == nullptr || (buf == nullptr && len > 0)) return VSA_ERR_INVALID_ARG;
+  static const char* const kRoute[] = {"VSA", "VSA_ALL_BLOCKS", "SDPA"};
+  static const char* const kMode[] = {"native", "dmd"};
+  static const char* const kReason[] = {"", "topk > num_blocks for the runtime shape",
+                                        "topk == num_blocks on a native checkpoint",
+                                        "unsupported problem: "};
+  if (r->route < 0 || r->route > 2 || r->checkpoint_mode < 0 || r->checkpoint_mode > 1 || r->reason < 0 ||
+      r->reason > 3)
+    return VSA_ERR_INVALID_ARG;
+  char tmp[768];
+  int n = 0;
+  if (r->has_plan) {
+    const vsa_plan_t& pl = r->plan;
+    const vsa_problem& p = pl.p;
+    const double keep = 100.0 * r->topk / pl.num_blocks;
+    n = std::snprintf(tmp, sizeof(tmp),
+                      "FASTVIDEO_VSA routing: seq_len=%lld, dit_seq_shape=(%d, %d, %d), block_size=(%d, %d, %d), "
+                      "num_blocks=%d, topk=%d, keep_ratio=%.1f%%, checkpoint_mode=%s, route=%s",
+                      (long long)pl.seq_len, p.latent[0], p.latent[1], p.latent[2], p.cube[0], p.cube[1],
+                      p.cube[2], pl.num_blocks, r->topk, keep, kMode[r->checkpoint_mode], kRoute[r->route]);
+  } else {
+    n = std::snprintf(tmp, sizeof(tmp), "FASTVIDEO_VSA routing: topk=%d, checkpoint_mode=%s, route=%s", r->topk,
+                      kMode[r->checkpoint_mode], kRoute[r->route]);
+  }
+  if (n < 0) return VSA_ERR_INVALID_ARG;
+  if (r->reason != VSA_REASON_NONE) {
+    const int m = std::snprintf(tmp + n, sizeof(tmp) - (size_t)n, ", reason=%s%s", kReason[r->reason],
+                                r->reason == VSA_REASON_UNSUPPORTED ? vsa_status_str(r->status) : "");
+    if (m < 0) return VSA_ERR_INVALID_ARG;
+    n += m;
+  }
+  if (len > 0) {
+    size_t c = (size_t)n < len - 1 ? (size_t)n : len - 1;
+    std::memcpy(buf, tmp, c);
+    buf[c] = '\0';
+  }
+  return n;
+}
+
 extern "C" const char* vsa_status_str(int s) {
   switch (s) {
     case VSA_OK: return "ok";

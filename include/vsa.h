@@ -179,6 +179,56 @@ int vsa_describe(const vsa_plan_t* plan, char* buf, size_t len);
 /* Static description of a status code; never NULL. */
 const char* vsa_status_str(int status);
 
+/* ---- Routing front end (user guide, sections "Wan top-k behavior" and
+ * "Verify routing and fallback"). Host only, no device work. The library
+ * itself never runs dense attention: a DENSE route tells the caller to run
+ * its own dense attention, for the reason given. */
+enum {
+  VSA_ROUTE_VSA = 0,             /* top-k block selection ("route=VSA")        */
+  VSA_ROUTE_VSA_ALL_BLOCKS = 1,  /* every block through the sparse kernels
+                                    ("route=VSA_ALL_BLOCKS")                   */
+  VSA_ROUTE_DENSE = 2            /* dense attention by the caller ("route=SDPA") */
+};
+enum {
+  VSA_CHECKPOINT_NATIVE = 0,     /* topk == num_blocks goes dense: scoring every
+                                    block gives no sparsity benefit            */
+  VSA_CHECKPOINT_DMD = 1         /* topk == num_blocks stays on the sparse
+                                    kernels (the checkpoint was trained with
+                                    them)                                     */
+};
+enum {
+  VSA_REASON_NONE = 0,
+  VSA_REASON_TOPK_ABOVE_BLOCKS = 1,  /* topk > num_blocks for this shape      */
+  VSA_REASON_ALL_BLOCKS_NATIVE = 2,  /* topk == num_blocks, native checkpoint */
+  VSA_REASON_UNSUPPORTED = 3         /* vsa_plan refused the problem; status
+                                        holds its code                        */
+};
+
+typedef struct vsa_route_t {
+  int32_t route;            /* VSA_ROUTE_*                                   */
+  int32_t reason;           /* VSA_REASON_*                                  */
+  int32_t status;           /* vsa_plan's status for VSA_REASON_UNSUPPORTED  */
+  int32_t checkpoint_mode;  /* as passed                                     */
+  int32_t topk;             /* as asked (may exceed plan.num_blocks)         */
+  int32_t has_plan;         /* 1: plan holds the problem's geometry (for a
+                               top-k above the block count, planned with
+                               topk = num_blocks); 0: no geometry            */
+  vsa_plan_t plan;          /* ready for vsa_select / vsa_attend when route
+                               is VSA or VSA_ALL_BLOCKS                      */
+} vsa_route_t;
+
+/* Decide the route of one problem. Returns VSA_OK and fills *out, or
+ * VSA_ERR_INVALID_ARG (null pointer, unknown checkpoint mode) or
+ * VSA_ERR_TOPK (topk < 1: a configuration error, not a fallback). */
+int vsa_route(const vsa_problem* problem, int32_t checkpoint_mode, vsa_route_t* out);
+
+/* The routing log line for a route ("FASTVIDEO_VSA routing: seq_len=...,
+ * ..., keep_ratio=..%, checkpoint_mode=native, route=VSA", with
+ * ", reason=..." on a dense route), the same fields and order as the user
+ * guide's Wan log. Writes into buf like vsa_describe and returns the full
+ * length, or a negative error code. */
+int vsa_describe_route(const vsa_route_t* route, char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -240,3 +240,60 @@ def test_topk_for_sparsity_matches_oracle():
     L = _lib.lib()
     for nb, s in ((120, 1.0), (120, -0.01), (120, float("nan")), (0, 0.5), (-3, 0.5)):
         assert L.vsa_topk_for_sparsity(nb, s) == _lib.VSA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# routing front end (user guide, "Wan top-k behavior" and "Verify routing
+# and fallback")
+# ---------------------------------------------------------------------------
+
+def test_route_wan_log_line():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "wan_routing_log.json")))
+    r = vsa.route(1, 24, 128, g["dit_seq_shape"], g["block_size"], g["topk"], checkpoint_mode=g["checkpoint_mode"])
+    assert r.route == g["route"] and r.reason == _lib.VSA_REASON_NONE and r.sparse
+    assert r.log_line() == (
+        "FASTVIDEO_VSA routing: seq_len={seq_len}, dit_seq_shape=({0}, {1}, {2}), block_size=({3}, {4}, {5}), "
+        "num_blocks={num_blocks}, topk={topk}, keep_ratio={keep_ratio}, checkpoint_mode={checkpoint_mode}, "
+        "route={route}".format(*g["dit_seq_shape"], *g["block_size"], **g))
+    assert r.plan.num_blocks == g["num_blocks"] and r.plan.topk == g["topk"]
+
+
+@pytest.mark.parametrize("topk,mode,route,reason", [
+    (64, "native", "VSA", _lib.VSA_REASON_NONE),
+    (64, "dmd", "VSA", _lib.VSA_REASON_NONE),
+    (1, "native", "VSA", _lib.VSA_REASON_NONE),
+    (119, "native", "VSA", _lib.VSA_REASON_NONE),
+    # topk == num_blocks: dense on a native checkpoint, all blocks on a DMD one
+    (120, "native", "SDPA", _lib.VSA_REASON_ALL_BLOCKS_NATIVE),
+    (120, "dmd", "VSA_ALL_BLOCKS", _lib.VSA_REASON_NONE),
+    # topk > num_blocks: invalid for the runtime shape, dense either way
+    (121, "native", "SDPA", _lib.VSA_REASON_TOPK_ABOVE_BLOCKS),
+    (500, "dmd", "SDPA", _lib.VSA_REASON_TOPK_ABOVE_BLOCKS),
+])
+def test_route_policy(topk, mode, route, reason):
+    r = vsa.route(1, 24, 128, (31, 22, 40), (4, 8, 8), topk, checkpoint_mode=mode)
+    assert (r.route, r.reason) == (route, reason)
+    assert r.plan is not None and r.plan.num_blocks == 120
+    assert r.plan.topk == min(topk, 120)
+    line = r.log_line()
+    assert f"topk={topk}," in line and f"checkpoint_mode={mode}, route={route}" in line
+    assert ("reason=" in line) == (reason != _lib.VSA_REASON_NONE)
+
+
+def test_route_unsupported_and_errors():
+    r = vsa.route(1, 24, 96, (31, 22, 40), (4, 8, 8), 64)
+    assert r.route == "SDPA" and r.reason == _lib.VSA_REASON_UNSUPPORTED
+    assert r.status == _lib.VSA_ERR_UNSUPPORTED and r.plan is None
+    assert "unsupported" in r.log_line()
+    r = vsa.route(1, 2, 128, (8, 8, 8), (4, 4, 4), 4, strides=(64 * 512 * 2, 64 * 512, 60))
+    assert r.route == "SDPA" and r.status == _lib.VSA_ERR_ALIGN
+    with pytest.raises(vsa.VsaError):
+        vsa.route(1, 24, 128, (31, 22, 40), (4, 8, 8), 0)      # top-k must be positive
+    with pytest.raises(ValueError):
+        vsa.route(1, 24, 128, (31, 22, 40), (4, 8, 8), 4, checkpoint_mode="gated")
+    L = _lib.lib()
+    pr = vsa.plan(1, 2, 128, (8, 8, 8), (4, 4, 4), 4).raw.p
+    out = _lib.VsaRoute()
+    assert L.vsa_route(ctypes.byref(pr), 5, ctypes.byref(out)) == _lib.VSA_ERR_INVALID_ARG
+    assert L.vsa_route(None, 0, ctypes.byref(out)) == _lib.VSA_ERR_INVALID_ARG
+    assert L.vsa_describe_route(None, None, 0) == _lib.VSA_ERR_INVALID_ARG
