@@ -49,6 +49,7 @@
 // c = head_dim^-1/2 * log2(e) and m a running bound of the scaled row max,
 // the same softmax.
 
+#include <atomic>
 #include <type_traits>
 
 #include "vsa_device.h"
@@ -334,10 +335,23 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 
   // ---- kept-block walk (issue side)
   const int nkept = gk.Pb + a.topk;
+  // Walk phase. The selected cubes are visited in ascending id order from a
+  // starting position rot, cyclically. With many small workgroups resident
+  // per XCD, a workgroup starts whenever an earlier one ends, so in steady
+  // state the resident set started at staggered times; a start position
+  // proportional to the dispatch index within the resident set keeps the
+  // cubes being read at any moment within a narrow band of cube ids, which
+  // the XCD's L2 then holds. The order only changes float rounding, and it
+  // depends on the launch alone, so results stay reproducible.
+  const int rot = a.walk_conc > 0
+                      ? (int)((int64_t)((blockIdx.x / 8) % (uint32_t)a.walk_conc) * a.topk / a.walk_conc)
+                      : 0;
   auto kept_block = [&](int i) -> int {
     if (i < gk.Pb) return i;
-    if (sel_lds) return gk.Pb + __builtin_amdgcn_readfirstlane(ssel[i - gk.Pb]);
-    int c = selrow[i - gk.Pb];
+    int t = i - gk.Pb + rot;
+    if (t >= a.topk) t -= a.topk;
+    if (sel_lds) return gk.Pb + __builtin_amdgcn_readfirstlane(ssel[t]);
+    int c = selrow[t];
     c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
     return gk.Pb + c;
   };
@@ -901,6 +915,29 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   }
 }
 
+// Workgroups of `func` resident at once on one XCD (8 per gfx950 device):
+// the occupancy per CU times the CUs of an XCD. Cached per device and LDS
+// size; -1 if a query fails.
+int resident_per_xcd(const void* func, int threads, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  // one atomic word per slot: a 48-bit key (never 0) over a 16-bit value
+  static std::atomic<uint64_t> cache[8];
+  uint64_t h = (uint64_t)(uintptr_t)func * 0x9E3779B97F4A7C15ull;
+  h ^= ((uint64_t)lds << 17) ^ ((uint64_t)threads << 3) ^ ((uint64_t)(uint32_t)dev << 40);
+  const uint64_t key = ((h >> 16) & 0xFFFFFFFFFFFFull) | 1ull;
+  std::atomic<uint64_t>& slot = cache[key % 8];
+  const uint64_t w = slot.load(std::memory_order_relaxed);
+  if ((w >> 16) == key) return (int)(w & 0xFFFFu);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, threads, lds) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  const int conc = per_cu * (cus / 8);
+  if (conc < 0 || conc > 0xFFFF) return -1;
+  slot.store((key << 16) | (uint64_t)conc, std::memory_order_relaxed);
+  return conc;
+}
+
 template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE, bool F16>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
@@ -918,7 +955,15 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   }
   const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * a.tiles;
   dim3 grid((unsigned)((nwg + 7) / 8 * 8));
-  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>), grid, dim3(NW * 64), lds, stream, a,
+  VsaArgs b = a;
+  b.walk_conc = 0;
+  if (!PIPE) {  // small-cube kernel: stagger the walks of the resident set
+    const int conc = resident_per_xcd(
+        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>), NW * 64, lds);
+    if (conc < 0) return hipErrorInvalidValue;
+    b.walk_conc = conc;
+  }
+  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>), grid, dim3(NW * 64), lds, stream, b,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();
 }
