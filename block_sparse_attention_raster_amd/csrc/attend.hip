@@ -138,6 +138,7 @@ struct Blk {
   int32_t ntiles;   // key tiles of the compact numbering
   int32_t ew, ehw;  // partial cubes: valid extents ew and eh*ew
   uint64_t mw, mhw; // and their division magics
+  int32_t type;     // video cubes: 2*[eh is the tail] + [ew is the tail]
   bool prefix;
   bool full;        // a whole cube (n == V) or a whole prefix block
 };
@@ -153,6 +154,7 @@ __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int
     d.ew = n;
     d.ehw = n;
     d.mw = d.mhw = 0;
+    d.type = 0;
     d.prefix = true;
     d.full = n == g.V;
     return d;
@@ -172,6 +174,7 @@ __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int
   d.ehw = eh * ew;
   d.mw = g.magic_ew[iw];
   d.mhw = g.magic_ehw[2 * ih + iw];
+  d.type = 2 * ih + iw;
   d.prefix = false;
   d.full = d.n == g.V;
   return d;
@@ -227,9 +230,10 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* kst = smem;                              // [NSTAGE][TILE_BYTES]
   unsigned char* vst = smem + NSTAGE * TILE_BYTES;        // [NSTAGE][TILE_BYTES]
-  int32_t* srel = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);  // [V]
   const VsaGrid& gk = a.gk;     // key/value side
-  int32_t* ssel = srel + gk.V;  // [topk] kept cubes, when topk <= VSA_ATTEND_SEL_LDS
+  // [4][V_k] row offsets of the compact slots of a key cube, by extent type
+  int32_t* stab = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);
+  int32_t* ssel = stab + 4 * gk.V;  // [topk] kept cubes, when a.sel_lds
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
   // id is remapped to give each XCD a contiguous range of (head, block) work.
@@ -248,18 +252,22 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   if (slot0 >= qd.n) return;
 
   const int tid = threadIdx.x;
-  {  // row offsets of a whole key cube's slots from its first row
-    const int chw = gk.ch * gk.cw;
-    for (int s = tid; s < gk.V; s += NW * 64) {
-      const int tt = s / chw;
-      const int rem = s - tt * chw;
-      const int hh = rem / gk.cw;
-      const int ww = rem - hh * gk.cw;
-      srel[s] = (tt * gk.H + hh) * gk.W + ww;
+  {  // Row offsets from a key cube's first row of its compact slots s, for
+     // the four extent types (eh, ew) in {ch, tail} x {cw, tail}: slot s is
+     // (tt, hh, ww) in raster order over the valid extents. Entries past a
+     // cube's token count are never used for a valid slot.
+    const int tail_h = gk.H - (gk.nH - 1) * gk.ch, tail_w = gk.W - (gk.nW - 1) * gk.cw;
+    for (int idx = tid; idx < 4 * gk.V; idx += NW * 64) {
+      const int t = idx / gk.V, s = idx - t * gk.V;
+      const int eh = (t >> 1) ? tail_h : gk.ch, ew = (t & 1) ? tail_w : gk.cw;
+      const int ehw = eh * ew;
+      const int tt = s / ehw, r = s - tt * ehw;
+      const int hh = r / ew, ww = r - hh * ew;
+      stab[idx] = (tt * gk.H + hh) * gk.W + ww;
     }
   }
   const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
-  const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS;
+  const bool sel_lds = a.sel_lds != 0;
   if (sel_lds) {
     for (int i = tid; i < a.topk; i += NW * 64) {
       const int c = selrow[i];
@@ -280,12 +288,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // token row of compact index k < d.n of key block d
   auto compact_row = [&](const Blk& d, int k) -> int {
     if (d.prefix) return d.base + k;
-    if (d.full) return d.base + srel[k];
-    const int tt = fast_div(k, d.mhw);
-    const int r = k - tt * d.ehw;
-    const int hh = fast_div(r, d.mw);
-    const int ww = r - hh * d.ew;
-    return d.base + (tt * gk.H + hh) * gk.W + ww;
+    return d.base + stab[d.type * gk.V + min(k, gk.V - 1)];
   };
   // token row of compact index k < d.n of the query block (q's grid; every
   // video cube, whole or partial, carries its extents' division magics)
@@ -406,33 +409,20 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // Pipelined kernel: the walker describes the next tile in scalar
   // registers outside the compute step (branches, block descriptors), and
   // the step itself forms the per-lane load addresses (branch-free vector
-  // work in its QK half, where the vector ALU is otherwise idle) and issues
-  // the copies, spread over its MFMA slots. Whole cubes with KT a multiple of
-  // ch*cw use this thread's row offsets within a tile, read from the slot
-  // table once here; other blocks unravel the compact index with
-  // multiply-high divisions (whole cubes too: their extents are the cube's).
+  // work, spread over its MFMA slots) and issues the copies. A video cube's
+  // slot rows come from the slot table of its extent type (one LDS read per
+  // load, issued several slots before the address is formed).
   struct Spec {
     int32_t base;    // first token row of the block
     int32_t nleft;   // valid slots from this tile on (KT or more: all)
     int32_t k0;      // compact index of the tile's first slot
-    int32_t trow;    // whole cubes: row offset of the tile
-    int32_t mode;    // 0 whole cube, 1 prefix, 2 unravel, 3 nothing left
-    int32_t ew, ehw;
-    uint64_t mw, mhw;
+    int32_t tbase;   // video cubes: first slot-table entry of its type
+    int32_t mode;    // 1 prefix, 2 video cube, 3 nothing left
   };
   struct Pend {
     uint32_t ko[SPW];              // K byte offsets from kh
     const unsigned char* va[SPW];  // V source addresses (zero row for tail slots)
   };
-  const int chw = gk.ch * gk.cw;
-  const bool fastshape = (KT % chw) == 0;
-  const int64_t tile_rows = (int64_t)(KT / chw) * gk.H * gk.W;
-  int srk[SPW];
-#pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int key = ((wave * SPW + j) * 64 + lane) / CPR;
-    srk[j] = (PIPE && fastshape && key < gk.V) ? srel[key] : 0;
-  }
   // describes the walker's current tile as ring slot AHEAD, then advances
   auto spec = [&](Spec& sp, uint64_t& m, bool& e) {
     const bool any = ibi < nkept;
@@ -440,12 +430,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     sp.base = any ? kd.base : 0;
     sp.nleft = any ? kd.n - t * KT : KT;
     sp.k0 = t * KT;
-    sp.trow = (int32_t)(t * tile_rows);
-    sp.mode = !any ? 3 : kd.prefix ? 1 : (kd.full && fastshape) ? 0 : 2;
-    sp.ew = kd.ew;
-    sp.ehw = kd.ehw;
-    sp.mw = kd.mw;
-    sp.mhw = kd.mhw;
+    sp.tbase = kd.type * gk.V;
+    sp.mode = !any ? 3 : kd.prefix ? 1 : 2;
     e = any;
     m = sp.nleft >= KT ? FULLM : ((1ull << sp.nleft) - 1ull);
     if (any) {
@@ -457,35 +443,47 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       }
     }
   };
-  // per-lane addresses of this thread's load j of the tile `sp` describes
-  auto addrs = [&](const Spec& sp, Pend& pd, int j) {
+  // Per-thread constants of load j (16-byte unit (wave*SPW + j)*64 + lane
+  // of a tile): its key slot, the swizzled chunk offsets in K and V, and the
+  // zero row's address for tail slots.
+  int keyj[SPW];
+  uint32_t kcst[SPW], vcst[SPW];
+  const unsigned char* zvj[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
     const int p = (wave * SPW + j) * 64 + lane;
     const int key = p / CPR, cp = p % CPR;
     const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+    keyj[j] = key;
+    kcst[j] = (uint32_t)((cp ^ (key & KSWZ)) * 16);
+    vcst[j] = (uint32_t)((cp ^ fv) * 16);
+    zvj[j] = reinterpret_cast<const unsigned char*>(vsa_zero_row) + vcst[j];
+  }
+  // slot-table entry of this thread's load j of the tile `sp` describes
+  // (clamped into the table: slots past the block's end are not used)
+  auto trow = [&](const Spec& sp, int j) -> int {
+    return stab[sp.tbase + min(sp.k0 + keyj[j], gk.V - 1)];
+  };
+  // per-lane addresses of this thread's load j of the tile `sp` describes,
+  // from its slot-table entry toff
+  auto addrs = [&](const Spec& sp, Pend& pd, int j, int toff) {
+    const int key = keyj[j];
     const bool valid = key < sp.nleft;
     const int kc = sp.k0 + key;
-    const int tt = fast_div(kc, sp.mhw);
-    const int r = kc - tt * sp.ehw;
-    const int hh = fast_div(r, sp.mw);
-    const int ww = r - hh * sp.ew;
-    // blend the three row formulas with opaque uniform masks: a select on a
-    // uniform condition would become a branch and split the fenced step
-    // (and the per-lane validity likewise: a divergent branch)
-    // Past the walker's last tile (mode 3) the extents are stale: row 0.
-    int m_pre = -(int)(sp.mode == 1), m_whole = -(int)(sp.mode == 0), m_val = -(int)valid;
-    int m_none = -(int)(sp.mode == 3);
-    asm volatile("" : "+v"(m_pre), "+v"(m_whole), "+v"(m_val), "+v"(m_none));
-    int row = sp.base + (tt * gk.H + hh) * gk.W + ww;
-    row = (row & ~m_pre) | ((sp.base + kc) & m_pre);
-    row = (row & ~m_whole) | ((sp.base + sp.trow + srk[j]) & m_whole);
+    // blend the row formulas with opaque masks: a select on a uniform
+    // condition would become a branch and split the fenced step (and the
+    // per-lane validity likewise: a divergent branch). Past the walker's
+    // last tile (mode 3) the block is stale: row 0.
+    int m_pre = -(int)(sp.mode == 1), m_val = -(int)valid, m_none = -(int)(sp.mode == 3);
+    asm volatile("" : "+v"(m_pre), "+v"(m_val), "+v"(m_none));
+    int row = sp.base + ((toff & ~m_pre) | (kc & m_pre));
     row = (row & m_val) | (sp.base & ~m_val);
     row &= ~m_none;
     // guard: never address past the last token row
     const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.ksn * 2u;
-    const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
-    pd.ko[j] = ro + (uint32_t)((cp ^ (key & KSWZ)) * 16);
-    const uint64_t vv = (uint64_t)reinterpret_cast<uintptr_t>(vh) + ro + vo;
-    const uint64_t vz = (uint64_t)reinterpret_cast<uintptr_t>(vsa_zero_row) + vo;
+    pd.ko[j] = ro + kcst[j];
+    const uint64_t vv = (uint64_t)reinterpret_cast<uintptr_t>(vh) + (ro + vcst[j]);
+    const uint64_t vz = (uint64_t)reinterpret_cast<uintptr_t>(zvj[j]);
     const uint64_t mv64 = (uint64_t)(int64_t)m_val;
     pd.va[j] = reinterpret_cast<const unsigned char*>((vv & mv64) | (vz & ~mv64));
   };
@@ -656,7 +654,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     bf16x8 kop[NQ];
     u32x2 vr[NDB][NVR];
     Pend pd;
-    static_assert(1 + 2 * (SPW - 1) < NQ / 2, "addresses before their copies");
+    int tv[SPW];
+    static_assert(1 + 2 * (SPW - 1) < NQ / 2, "table reads before their copies");
     float mx = 0.f, mc = 0.f, psum = 0.f;
 #pragma unroll
     for (int i = 0; i < KA; ++i) kop[i] = kread(ks, i / NC, i % NC);
@@ -671,12 +670,16 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       }
       const int kb = q / NC, c = q % NC;
       sa[kb] = E::mfma(kop[q], qreg[0][c], c == 0 ? f32x16{} : sa[kb]);
-      // the refill of the stage freed by this step's barrier: addresses of
-      // load j in slot 1 + 2j, its copies in slot NQ/2 + 2j
+      // the refill of the stage freed by this step's barrier: slot-table
+      // read of load j in slot 1 + 2j, its addresses and copies in slot
+      // NQ/2 + 2j
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
-        if (q == 1 + 2 * j) addrs(sp, pd, j);
-        if (q == NQ / 2 + 2 * j) fire(pd, fstage, j);
+        if (q == 1 + 2 * j) tv[j] = trow(sp, j);
+        if (q == NQ / 2 + 2 * j) {
+          addrs(sp, pd, j, tv[j]);
+          fire(pd, fstage, j);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -817,9 +820,12 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       Spec sp;
       auto fire_all = [&](int stage) {
         Pend pd;
+        int tv[SPW];
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) tv[j] = trow(sp, j);
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
-          addrs(sp, pd, j);
+          addrs(sp, pd, j, tv[j]);
           fire(pd, stage, j);
         }
       };
@@ -941,8 +947,10 @@ int resident_per_xcd(const void* func, int threads, size_t lds) {
 template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE, bool F16>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
-  const size_t lds = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.gk.V * 4 +
-                    (a.topk <= VSA_ATTEND_SEL_LDS ? (size_t)a.topk * 4 : 0);
+  // K and V stages, the four slot tables, and the kept list when it fits
+  const size_t lds_base = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.gk.V * 16;
+  const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS && lds_base + (size_t)a.topk * 4 <= 160 * 1024;
+  const size_t lds = lds_base + (sel_lds ? (size_t)a.topk * 4 : 0);
   if (lds > 65536) {
     static bool raised = false;  // benign race: the attribute call is idempotent
     if (!raised) {
@@ -956,6 +964,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * a.tiles;
   dim3 grid((unsigned)((nwg + 7) / 8 * 8));
   VsaArgs b = a;
+  b.sel_lds = sel_lds;
   b.walk_conc = 0;
   if (!PIPE) {  // small-cube kernel: stagger the walks of the resident set
     const int conc = resident_per_xcd(

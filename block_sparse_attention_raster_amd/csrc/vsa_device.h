@@ -56,6 +56,7 @@ struct VsaArgs {
   int32_t select_rows;   // query blocks per score/top-k workgroup
   int32_t tiles;         // query row tiles per query block
   int32_t f16;           // q, k, v, o are fp16 (else bf16)
+  int32_t sel_lds;       // attention: the kept-cube list is copied to LDS
   int32_t walk_conc;     // attention workgroups resident per XCD whose walks
                          // are phase-staggered (0: no stagger)
 };
