@@ -204,7 +204,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE, bool F16>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
                                                              const __bf16* __restrict__ k,
@@ -224,7 +224,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;
   static_assert(SLABS % NW == 0 && SPW >= 1, "tile loads must split evenly over the waves");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
-  static_assert(!PIPE || NSTAGE >= 3, "the pipelined loop keeps two tiles in use");
+  static_assert(NSTAGE >= 3, "the pipelined loop keeps two tiles in use");
   constexpr int VM_PER_TILE = 2 * SPW;   // vector-memory instructions per wave per tile
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -388,7 +388,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.ksn * 2u;
       const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
       dma16(kh, ro + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
-      if (!PIPE || nleft >= KT) {
+      if (nleft >= KT) {
         dma16(vh, ro + vo, lds_addr(vdst + s * 1024));
       } else {
         const unsigned char* vsrc = valid ? reinterpret_cast<const unsigned char*>(vh) + ro + vo
@@ -519,25 +519,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     return __builtin_bit_cast(u32x2, t);
   };
 
-  // S^T = K Q^T for the tile in `stage` (keys 32kb + ..., see the header)
-  auto qk = [&](int stage, f32x16 (&sacc)[QB][NKB]) {
-    bf16x8 kop[NKB][NC];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kop[kb][c] = kread(stage, kb, c);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = E::mfma(kop[kb][c], qreg[qb][c], sacc[qb][kb]);
-    }
-  };
-
   // O^T += V^T P^T for the tile in `stage`, one head-dim block of 32 at a time
   auto pv = [&](int stage, const bf16x8 (&pb)[QB][NKB][2]) {
 #pragma unroll
@@ -559,62 +540,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     }
   };
 
-  // Masked online softmax of one tile's scores, without branches on the
-  // common path. P goes out as bf16 operands. A row's exponent offset m is
-  // raised only when the tile's scaled max exceeds it by more than
-  // kRescaleLog2; alpha = 2^(m_old - m_new) (1 when unchanged) scales the
-  // row sum here and the O accumulators in `rescale`, after the P.V steps
-  // that still use the old scale. The row sum adds the bf16 P values that
-  // the P.V step multiplies (one v_dot2 per pair).
-  auto softmax = [&](f32x16 (&sacc)[QB][NKB], uint64_t cmask, bool masked, bf16x8 (&pb)[QB][NKB][2],
-                     float (&alpha)[QB]) {
-    if (masked) {
-      const uint64_t mg = cmask >> (4 * g);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const uint32_t mk = (uint32_t)(mg >> (32 * kb));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = 8 * (r >> 2) + (r & 3);
-          const bool valid = (mk >> bit) & 1u;
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sacc[qb][kb][r] = valid ? sacc[qb][kb][r] : -INFINITY;
-        }
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = sacc[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
-      const f32x2 hv = halves(mx);
-      mx = fmaxf(hv[0], hv[1]) * cexp;
-      const float mold = mrow[qb];
-      const float mc = mx > mold + kRescaleLog2 ? mx : mold;
-      alpha[qb] = __builtin_amdgcn_exp2f(mold - mc);
-      mrow[qb] = mc;
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 8 * hh + 2 * i;
-            // (a bit_cast of the vector element w[i] would read element 0)
-            const uint32_t pw = E::pack2(__builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r], cexp, -mc)),
-                                            __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][r + 1], cexp, -mc)));
-            psum = E::add2(pw, psum);
-            w[i] = pw;
-          }
-          pb[qb][kb][hh] = __builtin_bit_cast(bf16x8, w);
-        }
-      lrow[qb] = fmaf(lrow[qb], alpha[qb], psum);
-    }
-  };
   auto rescale = [&](const float (&alpha)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -655,7 +580,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     u32x2 vr[NDB][NVR];
     Pend pd;
     int tv[SPW];
-    static_assert(1 + 2 * (SPW - 1) < NQ / 2, "table reads before their copies");
+    // load j: slot-table read in slot rd_slot(j), addresses and copies in
+    // slot NQ/2 + fire_gap(j) (odd slots when there is room, else one load
+    // per slot)
+    static_assert(SPW <= NQ / 2, "one load per slot");
+    constexpr bool SPREAD = 1 + 2 * (SPW - 1) < NQ / 2;
+    auto rd_slot = [](int j) { return SPREAD ? 1 + 2 * j : (j * (NQ / 2)) / SPW; };
+    auto fire_gap = [](int j) { return SPREAD ? 2 * j : (j * (NQ / 2)) / SPW; };
     float mx = 0.f, mc = 0.f, psum = 0.f;
 #pragma unroll
     for (int i = 0; i < KA; ++i) kop[i] = kread(ks, i / NC, i % NC);
@@ -675,8 +606,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       // NQ/2 + 2j
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
-        if (q == 1 + 2 * j) tv[j] = trow(sp, j);
-        if (q == NQ / 2 + 2 * j) {
+        if (q == rd_slot(j)) tv[j] = trow(sp, j);
+        if (q == NQ / 2 + fire_gap(j)) {
           addrs(sp, pd, j, tv[j]);
           fire(pd, fstage, j);
         }
@@ -757,7 +688,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 
   // Tile ring: slot i holds the i-th tile from the one the next step starts
   // with. AHEAD tiles are in flight when a step begins.
-  constexpr int AHEAD = PIPE ? NSTAGE - 2 : NSTAGE - 1;
+  constexpr int AHEAD = NSTAGE - 2;
   uint64_t mring[AHEAD + 1];
   bool ering[AHEAD + 1];
 #pragma unroll
@@ -784,15 +715,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       wait_vmcnt<0>();
     }
   };
-  // refill ring slot AHEAD into `stage`, then the ring moves by one
-  auto refill = [&](int stage) {
-    if (ibi < nkept) {
-      mring[AHEAD] = issue(stage);
-      ering[AHEAD] = true;
-    } else {
-      ering[AHEAD] = false;
-    }
-  };
   auto shift = [&]() {
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) {
@@ -809,7 +731,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // accumulators in fixed registers.
   auto run = [&](auto active) {
     constexpr bool ACTIVE = decltype(active)::value;
-    if constexpr (PIPE) {
+    {
       // Software pipeline. Tile t sits in stage t % NSTAGE. Step j runs QK
       // of tile j and the P.V of tile j-1 (whose P the previous step made),
       // with the softmax of tile j on the vector ALUs while the P.V matrix
@@ -873,26 +795,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
         shift();
       }
-    } else {
-      int cur = 0;
-#pragma unroll 1
-      while (ering[0]) {
-        wait_first();
-        barrier();
-        // refill the stage freed by the previous tile
-        refill(cur == 0 ? NSTAGE - 1 : cur - 1);
-        if constexpr (ACTIVE) {
-          f32x16 sa[QB][NKB];
-          bf16x8 pb[QB][NKB][2];
-          float alpha[QB];
-          qk(cur, sa);
-          softmax(sa, mring[0], mring[0] != FULLM, pb, alpha);
-          rescale(alpha);
-          pv(cur, pb);
-        }
-        shift();
-        cur = cur + 1 == NSTAGE ? 0 : cur + 1;
-      }
     }
   };
   if (!wave_active) {
@@ -944,7 +846,7 @@ int resident_per_xcd(const void* func, int threads, size_t lds) {
   return conc;
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool PIPE, bool F16>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
   // K and V stages, the four slot tables, and the kept list when it fits
@@ -955,43 +857,46 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
     static bool raised = false;  // benign race: the attribute call is idempotent
     if (!raised) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>),
+          reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>),
           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
-  const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * a.tiles;
-  dim3 grid((unsigned)((nwg + 7) / 8 * 8));
   VsaArgs b = a;
+  constexpr int RW = NW * 32 * QB;  // query slots per workgroup
+  b.tiles = (a.gq.V + RW - 1) / RW;
+  const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * b.tiles;
+  if (nwg > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((nwg + 7) / 8 * 8));
   b.sel_lds = sel_lds;
   b.walk_conc = 0;
-  if (!PIPE) {  // small-cube kernel: stagger the walks of the resident set
+  if (NW == 2) {  // small-cube kernel: stagger the walks of the resident set
     const int conc = resident_per_xcd(
-        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>), NW * 64, lds);
+        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), NW * 64, lds);
     if (conc < 0) return hipErrorInvalidValue;
     b.walk_conc = conc;
   }
-  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, PIPE, F16>), grid, dim3(NW * 64), lds, stream, b,
+  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), grid, dim3(NW * 64), lds, stream, b,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Tilings: cubes of up to 64 tokens use 2-wave workgroups (64 query rows)
-// with 32-key tiles, so four workgroups share a CU and each SIMD runs two
-// independent waves; larger cubes use 8-wave workgroups (256 query rows)
-// with 64-key tiles four stages deep and the software-pipelined step.
+// Tilings, all on the pipelined step: cubes of up to 64 tokens use 2-wave
+// workgroups (64 query rows) with 32-key tiles three stages deep, so three
+// workgroups share a CU; larger cubes use 8-wave workgroups (256 query rows)
+// with 64-key tiles four stages deep.
 template <bool F16>
 static hipError_t dispatch(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                            const int32_t* sel, void* o, hipStream_t stream) {
   if (a.D == 128) {
-    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, false, F16>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, 4, 64, 2, true, F16>(a, q, k, v, sel, o, stream);
+    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 3, 32, 2, F16>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 1, 4, 64, 2, F16>(a, q, k, v, sel, o, stream);
   }
-  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, false, F16>(a, q, k, v, sel, o, stream);
-  return launch<64, 8, 1, 4, 64, 2, true, F16>(a, q, k, v, sel, o, stream);
+  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 3, 32, 2, F16>(a, q, k, v, sel, o, stream);
+  return launch<64, 8, 1, 4, 64, 2, F16>(a, q, k, v, sel, o, stream);
 }
 
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
