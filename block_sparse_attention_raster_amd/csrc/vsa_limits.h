@@ -3,7 +3,9 @@
 #define VSA_LIMITS_H
 
 #define VSA_MAX_CUBE_VOLUME 1024      /* tokens per block                      */
-#define VSA_MAX_BLOCKS 16384          /* video cubes per (batch, head)         */
+#define VSA_MAX_BLOCKS 4096           /* video cubes per (batch, head): four
+                                         score rows of 4096 keys fill the
+                                         selection LDS budget               */
 #define VSA_SELECT_MAX_ROWS 16        /* query blocks per score/top-k group    */
 #define VSA_SELECT_SCORE_LDS 65536    /* bytes of LDS for one group's scores   */
 #define VSA_SELECT_MFMA_MAX_BLOCKS 2048 /* cubes scored on the matrix cores    */

@@ -68,7 +68,7 @@ enum {
                                 guide: top-k must be positive and may not
                                 exceed the block count)                     */
   VSA_ERR_UNSUPPORTED = -3,  /* head_dim not 64 or 128, dtype unknown,  
-                                cube volume > 1024, num_blocks > 16384      */
+                                cube volume > 1024, num_blocks > 4096       */
   VSA_ERR_ALIGN = -4,        /* pointer or stride not 16-byte aligned       */
   VSA_ERR_OVERFLOW = -5,     /* an element offset or a count would overflow
                                 the kernels' index types                    */

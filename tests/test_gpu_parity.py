@@ -78,6 +78,12 @@ SMALL = [
     ("tail_extents_1_2", 1, 2, 128, (5, 9, 18), (4, 8, 8), 4, 0),
     # tail tiles with more than 32 valid slots (a mask word of all ones)
     ("tail_tile_40", 1, 2, 128, (5, 13, 16), (4, 8, 8), 3, 40),
+    # the largest cube volume (1024 tokens: four 256-row query tiles per
+    # cube), partial on every axis
+    ("cube_v1024", 1, 2, 128, (9, 20, 35), (4, 16, 16), 3, 0),
+    # a cube volume between the tilings (330 tokens: two query tiles) with
+    # partial prefix and cubes
+    ("cube_v330", 1, 2, 64, (7, 12, 13), (3, 10, 11), 2, 17),
 ]
 
 
@@ -103,6 +109,31 @@ def test_many_cubes_vector_select_path():
     w = synthetic.custom_workload("many_cubes", seed=12, batch=1, heads=2, head_dim=64,
                                   latent=(16, 24, 48), cube=(2, 2, 2), topk=16)
     _full_check(w, 16, blocks_per_head=10)
+
+
+@pytest.mark.parametrize("topk", [3000, 4096])
+def test_max_blocks(topk):
+    """The largest cube count (4096 cubes of 16 tokens, 65536 tokens) with
+    long kept lists, up to every cube: selection checked on 256 sampled
+    rows, outputs on sampled query blocks."""
+    w = synthetic.custom_workload("max_blocks", seed=41, batch=1, heads=1, head_dim=64,
+                                  latent=(32, 32, 64), cube=(2, 2, 4), topk=topk)
+    _announce(f"max blocks: 4096 cubes, topk {topk}")
+    res = G.run_gpu(w, topk)
+    assert res["plan"].num_blocks == 4096
+    g = O.geometry(w.latent, w.cube)
+    q_b, k_b, _ = res["bits"]
+    qbar = O.pool(O.decode_bf16(q_b[0, 0]), g)
+    kbar = O.pool(O.decode_bf16(k_b[0, 0]), g, video_only=True)
+    np.testing.assert_allclose(res["kbar"][0, 0], kbar, rtol=1e-5, atol=1e-5)
+    rng = np.random.default_rng(41)
+    rows = np.unique(np.concatenate([rng.choice(g.num_q_blocks, 254, replace=False), [0, g.num_q_blocks - 1]]))
+    scores = O.block_scores(qbar[rows], kbar, w.head_dim)
+    chk = O.check_selection(res["sel"][0, 0][rows], scores, topk, band=G.TIE_BAND)
+    assert chk["mismatch_rows"] == [], chk["mismatch_rows"][:10]
+    worst = G.check_outputs(w, g, res, [(0, 0)], blocks_per_head=4)
+    _announce(f"max blocks/topk{topk}: max_abs {worst['max_abs']:.3e} rel_l2 {worst['rel_l2']:.3e}")
+    assert worst["max_abs"] <= G.MAX_ABS and worst["rel_l2"] <= G.REL_L2, worst
 
 
 def test_all_blocks_equals_dense_attention():
