@@ -5,22 +5,25 @@
 //
 // Work split. One workgroup owns RW = NW*32*QB query slots of one query block
 // of one (batch, head); each wave owns 32*QB of them. The kept key blocks
-// (all prefix blocks, then the selected cubes in ascending order) are walked
-// in tiles of 64 key slots.
+// (all prefix blocks, then the selected cubes in ascending id order, cyclic
+// from a start chosen per workgroup) are walked in tiles of KT key slots.
 //
 // Index map (fastbsa package page, section "How it works": the raster to
 // block map is evaluated inside the kernel). The n valid tokens of a block
 // are numbered k = (tt*eh + hh)*ew + ww over its valid extents (et, eh, ew)
 // (partial cubes at the far edge of an axis have smaller extents); prefix
 // block tokens are rows p*V + k. Both query rows and key tiles walk this
-// compact numbering, so a block of n tokens fills floor(n/64) whole key
-// tiles and at most one tail tile, whose slots past n load the block's first
-// row (finite data) and are masked to -inf. For whole key cubes the
-// workgroup tabulates each k's row offset (tt*H + hh)*W + ww from the cube's
-// first token at start-up (one LDS read per row); partial cubes, and query
-// rows, unravel k with multiply-high divisions by eh*ew and ew. Query blocks
-// follow q's grid and cube shape, key blocks k's (the two differ when q and
-// k/v lie on different grids: fastbsa package page, section "Use").
+// compact numbering, so a block of n tokens fills floor(n/KT) whole key
+// tiles and at most one tail tile. A tail tile's slots past n load the
+// block's first row for K and a zero row for V, so they need no masking: a
+// correction after the step removes them from the row sum. The row offset
+// (tt*H + hh)*W + ww of slot k depends only on the extents, which take four
+// values per grid (whole or tail along h and along w), so the workgroup
+// tabulates the four maps of the key grid at start-up and each load reads
+// its row offset from LDS; query rows (read once) unravel k with
+// multiply-high divisions. Query blocks follow q's grid and cube shape, key
+// blocks k's (the two differ when q and k/v lie on different grids:
+// fastbsa package page, section "Use").
 //
 // Data movement. K and V tiles go from HBM straight into LDS with 16-byte
 // global_load_lds (no registers), NSTAGE tiles deep; each wave issues its
