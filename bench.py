@@ -36,10 +36,18 @@ ATTEND_SOURCES = ["attend.hip", "vsa_device.h", "vsa_limits.h"]
 
 
 def attend_source_hash() -> str:
+    """Hash of the attention kernel's sources with comments and blank lines
+    removed, so that the recorded traffic stays valid across comment edits
+    and lapses when the code changes."""
+    import re
     h = hashlib.sha256()
     for s in ATTEND_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_attention_raster_amd", "csrc", s), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_attention_raster_amd", "csrc", s)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.rstrip() for line in text.split("\n") if line.strip())
+        h.update(text.encode())
     return h.hexdigest()
 
 
