@@ -286,15 +286,16 @@ __global__ __launch_bounds__(kSelThreads) void vsa_score_topk_kernel(VsaArgs a, 
 
 // Scores on the fp32 matrix cores (v_mfma_f32_16x16x4f32) for up to
 // VSA_SELECT_MFMA_MAX_BLOCKS cubes: one workgroup takes 16 query blocks of one head; each
-// wave takes every fourth block of 16 cubes. In one MFMA step, lane group
+// wave takes every eighth block of 16 cubes. In one MFMA step, lane group
 // g = lane/16 contributes head-dim index D/4*g + c, so each lane's operands
 // are a contiguous quarter of one qbar or kbar row, loaded as float4 straight
 // from global memory (L2-resident). The 16x16 result lands as keys in LDS;
-// then each wave runs row_topk on four rows.
+// then each of the eight waves runs row_topk on two rows.
 constexpr int kMfmaRows = 16;
+constexpr int kMfmaWaves = 8;  // two rows per wave in the top-k phase
 
 template <int D, int KPL>
-__global__ __launch_bounds__(kSelThreads) void vsa_score_topk_mfma_kernel(VsaArgs a, const float* __restrict__ qbar,
+__global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(VsaArgs a, const float* __restrict__ qbar,
                                                                           const float* __restrict__ kbar,
                                                                           int32_t* __restrict__ sel) {
   constexpr int DQ = D / 4;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kSelThreads) void vsa_score_topk_mfma_kernel(VsaArg
     }
   }
   const float* kbase = kbar + (int64_t)bh * a.nb * D + DQ * g;
-  for (int cb = wave; cb * 16 < a.nb; cb += kSelWaves) {
+  for (int cb = wave; cb * 16 < a.nb; cb += kMfmaWaves) {
     const int col = cb * 16 + l16;
     const bool ok = col < a.nb;
     const f32x4* src = reinterpret_cast<const f32x4*>(kbase + (int64_t)(ok ? col : 0) * D);
@@ -349,14 +350,14 @@ __global__ __launch_bounds__(kSelThreads) void vsa_score_topk_mfma_kernel(VsaArg
   }
   __syncthreads();
   uint32_t* wh = hist + wave * 256;
-  for (int r = wave; r < nrows; r += kSelWaves)
+  for (int r = wave; r < nrows; r += kMfmaWaves)
     row_topk_regs<KPL>(sc + r * a.nb, a.nb, a.topk, wh, lane, sel + ((int64_t)bh * a.nq + row0 + r) * a.topk);
 }
 
 }  // namespace
 
 size_t vsa_select_lds_bytes(const VsaArgs& a) {
-  if (a.nb <= VSA_SELECT_MFMA_MAX_BLOCKS) return (size_t)kMfmaRows * a.nb * 4 + (size_t)kSelWaves * 256 * 4;
+  if (a.nb <= VSA_SELECT_MFMA_MAX_BLOCKS) return (size_t)kMfmaRows * a.nb * 4 + (size_t)kMfmaWaves * 256 * 4;
   return (size_t)a.select_rows * a.D * 4 + (size_t)kColChunk * a.D * 4 + (size_t)kSelWaves * 256 * 4 +
          (size_t)a.select_rows * a.nb * 4;
 }
@@ -401,7 +402,7 @@ hipError_t launch_mfma_kpl(const VsaArgs& a, const float* qbar, const float* kba
     raised.store(1, std::memory_order_release);
   }
   const int groups = (a.nq + kMfmaRows - 1) / kMfmaRows;
-  hipLaunchKernelGGL((vsa_score_topk_mfma_kernel<D, KPL>), dim3(groups * a.B * a.Hh), dim3(kSelThreads), lds,
+  hipLaunchKernelGGL((vsa_score_topk_mfma_kernel<D, KPL>), dim3(groups * a.B * a.Hh), dim3(kMfmaWaves * 64), lds,
                      stream, a, qbar, kbar, sel);
   return hipGetLastError();
 }
