@@ -139,11 +139,10 @@ struct Blk {
   int32_t base;     // first token row (the row of index 0)
   int32_t n;        // valid tokens
   int32_t ntiles;   // key tiles of the compact numbering
-  int32_t ew, ehw;  // partial cubes: valid extents ew and eh*ew
+  int32_t ew, ehw;  // valid extents ew and eh*ew (query rows unravel with them)
   uint64_t mw, mhw; // and their division magics
   int32_t type;     // video cubes: 2*[eh is the tail] + [ew is the tail]
   bool prefix;
-  bool full;        // a whole cube (n == V) or a whole prefix block
 };
 
 __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int32_t kt) {
@@ -159,7 +158,6 @@ __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int
     d.mw = d.mhw = 0;
     d.type = 0;
     d.prefix = true;
-    d.full = n == g.V;
     return d;
   }
   const int32_t c = blk - g.Pb;
@@ -179,7 +177,6 @@ __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int
   d.mhw = g.magic_ehw[2 * ih + iw];
   d.type = 2 * ih + iw;
   d.prefix = false;
-  d.full = d.n == g.V;
   return d;
 }
 
