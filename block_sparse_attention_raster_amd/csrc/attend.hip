@@ -26,9 +26,12 @@
 // fastbsa package page, section "Use").
 //
 // Data movement. K and V tiles go from HBM straight into LDS with 16-byte
-// global_load_lds (no registers), NSTAGE tiles deep; each wave issues its
-// share, waits for its own loads of the tile about to be used, and one
-// barrier per tile publishes it and frees the stage the next issue reuses.
+// global_load_lds (no registers) into two rings of NSTAGE tiles each. Step s
+// reads K of tile s and V of tile s-1, so the copies of a tile's V are
+// issued one step after its K: step s issues K of tile s+NSTAGE-1 and V of
+// tile s+NSTAGE-2, each into the stage the previous step finished with.
+// Each wave issues its share, waits for its own copies of what the next
+// step reads, and one barrier per tile publishes them.
 // Both tiles keep the natural [key][head_dim] order with the 16-byte chunks
 // of each key row XOR-swizzled (applied on the global side, since the LDS
 // position of each lane's 16 bytes is fixed by its lane id).
@@ -223,8 +226,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   constexpr int TILE_BYTES = UNITS * 16;
   constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;
   static_assert(SLABS % NW == 0 && SPW >= 1, "tile loads must split evenly over the waves");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
-  static_assert(NSTAGE >= 3, "the pipelined loop keeps two tiles in use");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
   constexpr int VM_PER_TILE = 2 * SPW;   // vector-memory instructions per wave per tile
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -370,10 +372,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // registers across the compute steps.
   // Issues the loads of the walker's current tile into `stage` and returns
   // its validity mask (bit i: slot i of the tile is valid); then advances.
-  auto issue = [&](int stage) -> uint64_t {
+  // K of the walker's current tile into `stage` now; its V addresses go to
+  // vpend, and fire_v issues them one step later (V of a tile is first read
+  // one step after its K). Returns the tile's validity mask (bit i: slot i
+  // is valid), then advances the walker.
+  const unsigned char* vpend[SPW];
+  auto issue_k = [&](int stage) -> uint64_t {
     const int t = ikt;
     unsigned char* kdst = kst + stage * TILE_BYTES;
-    unsigned char* vdst = vst + stage * TILE_BYTES;
     const int nleft = kd.n - t * KT;          // valid slots from this tile on
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -388,13 +394,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.ksn * 2u;
       const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
       dma16(kh, ro + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
-      if (nleft >= KT) {
-        dma16(vh, ro + vo, lds_addr(vdst + s * 1024));
-      } else {
-        const unsigned char* vsrc = valid ? reinterpret_cast<const unsigned char*>(vh) + ro + vo
-                                          : reinterpret_cast<const unsigned char*>(vsa_zero_row) + vo;
-        dma16(vsrc, lds_addr(vdst + s * 1024));
-      }
+      vpend[j] = valid ? reinterpret_cast<const unsigned char*>(vh) + ro + vo
+                       : reinterpret_cast<const unsigned char*>(vsa_zero_row) + vo;
     }
     const uint64_t m = nleft >= KT ? FULLM : __ballot(lane < nleft);
     ++ikt;
@@ -404,6 +405,10 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       if (ibi < nkept) kd = describe_block(gk, kept_block(ibi), KT);
     }
     return m;
+  };
+  auto fire_v = [&](int stage, int j) {
+    const int s = wave * SPW + j;
+    dma16(vpend[j], lds_addr(vst + stage * TILE_BYTES + s * 1024));
   };
 
   // Pipelined kernel: the walker describes the next tile in scalar
@@ -487,10 +492,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     const uint64_t mv64 = (uint64_t)(int64_t)m_val;
     pd.va[j] = reinterpret_cast<const unsigned char*>((vv & mv64) | (vz & ~mv64));
   };
-  auto fire = [&](const Pend& pd, int stage, int j) {
+  // load j of a refill: V of tile s + AHEAD - 1 (addresses from the step
+  // before) into vstage, then K of tile s + AHEAD into kstage, whose V
+  // addresses replace the ones just used
+  auto fire = [&](const Pend& pd, int kstage, int vstage, int j) {
     const int s = wave * SPW + j;
-    dma16(kh, pd.ko[j], lds_addr(kst + stage * TILE_BYTES + s * 1024));
-    dma16(pd.va[j], lds_addr(vst + stage * TILE_BYTES + s * 1024));
+    fire_v(vstage, j);
+    dma16(kh, pd.ko[j], lds_addr(kst + kstage * TILE_BYTES + s * 1024));
+    vpend[j] = pd.va[j];
   };
 
   // per-lane LDS offsets of the MFMA operands
@@ -563,7 +572,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // max has already seen (or sees in this tile), and their V rows are zero;
   // `tail_sum` then removes those slots from the row sum.
   auto step = [&](auto with_pv, int ks, int vs_, const bf16x8 (&pb)[QB][NKB][2], bf16x8 (&pn)[QB][NKB][2],
-                  float (&alpha)[QB], const Spec& sp, int fstage) {
+                  float (&alpha)[QB], const Spec& sp, int kstage, int vstage) {
     constexpr bool WITH_PV = decltype(with_pv)::value;
     static_assert(QB == 1, "the fixed schedule is written for one query block per wave");
     constexpr int KA = 6;                   // K reads ahead of their MFMA
@@ -609,7 +618,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         if (q == rd_slot(j)) tv[j] = trow(sp, j);
         if (q == NQ / 2 + fire_gap(j)) {
           addrs(sp, pd, j, tv[j]);
-          fire(pd, fstage, j);
+          fire(pd, kstage, vstage, j);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -688,7 +697,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 
   // Tile ring: slot i holds the i-th tile from the one the next step starts
   // with. AHEAD tiles are in flight when a step begins.
-  constexpr int AHEAD = NSTAGE - 2;
+  constexpr int AHEAD = NSTAGE - 1;
   uint64_t mring[AHEAD + 1];
   bool ering[AHEAD + 1];
 #pragma unroll
@@ -696,14 +705,22 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     ering[i] = false;
     mring[i] = 0;
   }
+  // prologue: K of tiles 0 .. AHEAD-1 and V of tiles 0 .. AHEAD-2, in the
+  // order the steps would issue them
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) {
+    if (i > 0 && ering[i - 1]) {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) fire_v(i - 1, j);
+    }
     if (ibi < nkept) {
-      mring[i] = issue(i);
+      mring[i] = issue_k(i);
       ering[i] = true;
     }
   }
-  // wait for this wave's loads of ring slot 0 (later tiles may stay in flight)
+  // wait for this wave's copies of the K of ring slot 0 and of the V of the
+  // tile before it (both issued in the same step; later ones may stay in
+  // flight)
   auto wait_first = [&]() {
     if constexpr (AHEAD >= 3) {
       if (ering[2]) wait_vmcnt<2 * VM_PER_TILE>();
@@ -740,7 +757,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       // of tile j + NSTAGE - 2 into it (prepared before the barrier).
       bf16x8 pb[QB][NKB][2];
       Spec sp;
-      auto fire_all = [&](int stage) {
+      auto fire_all = [&](int kstage, int vstage) {
         Pend pd;
         int tv[SPW];
 #pragma unroll
@@ -748,7 +765,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
           addrs(sp, pd, j, tv[j]);
-          fire(pd, stage, j);
+          fire(pd, kstage, vstage, j);
         }
       };
       // first tile: QK and softmax only (every kept list has a tile)
@@ -757,11 +774,11 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       barrier();
       if constexpr (ACTIVE) {
         float alpha[QB];
-        step(F_{}, 0, 0, pb, pb, alpha, sp, AHEAD);
+        step(F_{}, 0, 0, pb, pb, alpha, sp, AHEAD, AHEAD - 1);
         if (mring[0] != FULLM) tail_sum(mring[0], pb);
         rescale(alpha);
       } else {
-        fire_all(AHEAD);
+        fire_all(AHEAD, AHEAD - 1);
       }
       shift();
       int cur = 1, prev = 0;
@@ -769,9 +786,11 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 #pragma unroll 1
       while (true) {
         const bool have = ering[0];
-        const int fst = cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD;
+        const int fst = cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD;   // K refill
+        const int vfst = fst == 0 ? NSTAGE - 1 : fst - 1;                               // V refill
         if (have) spec(sp, mring[AHEAD], ering[AHEAD]);
-        if (have) wait_first();
+        // the last P.V reads V of the last tile, copied one step after its K
+        if (have) wait_first(); else wait_vmcnt<0>();
         barrier();
         if (!have) {
           if constexpr (ACTIVE) pv(prev, pb);
@@ -780,7 +799,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         if constexpr (ACTIVE) {
           bf16x8 pn[QB][NKB][2];
           float alpha[QB];
-          step(T_{}, cur, prev, pb, pn, alpha, sp, fst);
+          step(T_{}, cur, prev, pb, pn, alpha, sp, fst, vfst);
           if (mring[0] != FULLM) tail_sum(mring[0], pn);
           rescale(alpha);
 #pragma unroll
@@ -789,7 +808,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
             pb[0][kb][1] = pn[0][kb][1];
           }
         } else {
-          fire_all(fst);
+          fire_all(fst, vfst);
         }
         prev = cur;
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
@@ -885,18 +904,18 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
 }  // namespace
 
 // Tilings, all on the pipelined step: cubes of up to 64 tokens use 2-wave
-// workgroups (64 query rows) with 32-key tiles three stages deep, so three
-// workgroups share a CU; larger cubes use 8-wave workgroups (256 query rows)
-// with 64-key tiles four stages deep.
+// workgroups (64 query rows) with 32-key tiles in rings of two (32 KB of LDS
+// for D = 128, so four workgroups share a CU); larger cubes use 8-wave
+// workgroups (256 query rows) with 64-key tiles in rings of three.
 template <bool F16>
 static hipError_t dispatch(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                            const int32_t* sel, void* o, hipStream_t stream) {
   if (a.D == 128) {
-    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 3, 32, 2, F16>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, 4, 64, 2, F16>(a, q, k, v, sel, o, stream);
+    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, F16>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 1, 3, 64, 2, F16>(a, q, k, v, sel, o, stream);
   }
-  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 3, 32, 2, F16>(a, q, k, v, sel, o, stream);
-  return launch<64, 8, 1, 4, 64, 2, F16>(a, q, k, v, sel, o, stream);
+  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, F16>(a, q, k, v, sel, o, stream);
+  return launch<64, 8, 1, 3, 64, 2, F16>(a, q, k, v, sel, o, stream);
 }
 
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
