@@ -407,3 +407,89 @@ def test_two_grids_api_with_equal_grids_is_bitwise_the_same():
                         cube_shape_k=w.cube)
     torch.cuda.synchronize()
     assert torch.equal(sa, sb) and torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# execution properties: the C entry point vsa_forward, concurrent streams,
+# HIP graph capture
+# ---------------------------------------------------------------------------
+
+def _small_problem(seed=51, latent=(5, 9, 17), cube=(4, 8, 8), topk=3, prefix=20, heads=2):
+    import torch
+    import block_sparse_attention_raster_amd as vsa
+    w = synthetic.custom_workload("exec", seed=seed, batch=1, heads=heads, head_dim=128,
+                                  latent=latent, cube=cube, topk=topk, prefix_len=prefix)
+    q, k, v = (G.to_device(x) for x in synthetic.make_inputs(w))
+    pl = vsa.plan_for(q, w.latent, w.cube, topk, prefix)
+    ws = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device="cuda")
+    sel = torch.empty(pl.sel_elems, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    return pl, q, k, v, ws, sel, out
+
+
+def test_vsa_forward_entry_point_matches_select_then_attend():
+    import ctypes
+    import torch
+    import block_sparse_attention_raster_amd as vsa
+    from block_sparse_attention_raster_amd import _lib
+    _announce("vsa_forward through the C ABI")
+    pl, q, k, v, ws, sel, out = _small_problem()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = _lib.lib().vsa_forward(ctypes.byref(pl.raw), q.data_ptr(), k.data_ptr(), v.data_ptr(), ws.data_ptr(),
+                                sel.data_ptr(), out.data_ptr(), st)
+    assert rc == _lib.VSA_OK
+    sel2, _ = vsa.select(pl, q, k)
+    out2 = vsa.attend(pl, q, k, v, sel2)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.view_as(sel2), sel2) and torch.equal(out, out2)
+
+
+def test_concurrent_streams_give_the_sequential_results():
+    """Two different problems on two streams at once: the library keeps no
+    per-call state, so each matches its own sequential run bit for bit."""
+    import torch
+    import block_sparse_attention_raster_amd as vsa
+    _announce("two streams")
+    a = _small_problem(seed=52)
+    b = _small_problem(seed=53, latent=(6, 8, 10), cube=(4, 4, 4), topk=5, prefix=0, heads=3)
+    ref = []
+    for pl, q, k, v, ws, sel, out in (a, b):
+        s_, _ = vsa.select(pl, q, k)
+        ref.append(vsa.attend(pl, q, k, v, s_))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        for (pl, q, k, v, ws, sel, out), st in zip((a, b), streams):
+            with torch.cuda.stream(st):
+                vsa.select(pl, q, k, ws, sel.view(pl.batch, pl.heads, pl.num_q_blocks, pl.topk))
+                vsa.attend(pl, q, k, v, sel.view(pl.batch, pl.heads, pl.num_q_blocks, pl.topk), out)
+        torch.cuda.synchronize()
+        assert torch.equal(a[6], ref[0]) and torch.equal(b[6], ref[1])
+
+
+def test_hip_graph_capture_and_replay():
+    """select + attend captured into one HIP graph (no allocation, no
+    synchronisation inside the calls) and replayed several times, with eager
+    work between replays; every replay equals the eager result."""
+    import torch
+    import block_sparse_attention_raster_amd as vsa
+    _announce("HIP graph capture")
+    pl, q, k, v, ws, sel, out = _small_problem(seed=54)
+    sel4 = sel.view(pl.batch, pl.heads, pl.num_q_blocks, pl.topk)
+    vsa.select(pl, q, k, ws, sel4)
+    vsa.attend(pl, q, k, v, sel4, out)
+    torch.cuda.synchronize()
+    ref, ref_sel = out.clone(), sel.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        vsa.select(pl, q, k, ws, sel4)
+        vsa.attend(pl, q, k, v, sel4, out)
+    for i in range(4):
+        out.zero_()
+        sel.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        assert torch.equal(sel, ref_sel), f"replay {i}"
+        _ = (q.float() * 2).sum().item()      # eager work between replays
