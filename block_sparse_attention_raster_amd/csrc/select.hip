@@ -287,9 +287,10 @@ __global__ __launch_bounds__(kSelThreads) void vsa_score_topk_kernel(VsaArgs a, 
 // Scores on the fp32 matrix cores (v_mfma_f32_16x16x4f32) for up to
 // VSA_SELECT_MFMA_MAX_BLOCKS cubes: one workgroup takes 16 query blocks of one head; each
 // wave takes every eighth block of 16 cubes. In one MFMA step, lane group
-// g = lane/16 contributes head-dim index D/4*g + c, so each lane's operands
-// are a contiguous quarter of one qbar or kbar row, loaded as float4 straight
-// from global memory (L2-resident). The 16x16 result lands as keys in LDS;
+// g = lane/16 contributes head-dim index 16*(c/4) + 4*g + c%4, so one
+// 16-byte load instruction reads 64 contiguous bytes of each of 16 qbar or
+// kbar rows, straight from global memory (L2-resident: workgroups of one
+// head run on one XCD). The 16x16 result lands as keys in LDS;
 // then each of the eight waves runs row_topk on two rows.
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaWaves = 8;  // two rows per wave in the top-k phase
@@ -304,8 +305,15 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(Vs
   uint32_t* hist = sc + kMfmaRows * a.nb;               // [waves][256]
 
   const int groups = (a.nq + kMfmaRows - 1) / kMfmaRows;
-  const int bh = blockIdx.x / groups;
-  const int row0 = (blockIdx.x - bh * groups) * kMfmaRows;
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
+  // id is remapped to give each XCD a contiguous range (whole heads): a
+  // head's kbar then stays in one XCD's L2
+  const int nwg = groups * a.B * a.Hh;
+  const int per_xcd = (nwg + 7) / 8;
+  const int lid = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (lid >= nwg) return;
+  const int bh = lid / groups;
+  const int row0 = (lid - bh * groups) * kMfmaRows;
   const int nrows = min(kMfmaRows, a.nq - row0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
@@ -313,17 +321,17 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(Vs
   float qv[DQ];
   {
     const bool ok = l16 < nrows;
-    const f32x4* src = reinterpret_cast<const f32x4*>(qbar + ((int64_t)bh * a.nq + row0 + (ok ? l16 : 0)) * D + DQ * g);
+    const f32x4* src = reinterpret_cast<const f32x4*>(qbar + ((int64_t)bh * a.nq + row0 + (ok ? l16 : 0)) * D + 4 * g);
 #pragma unroll
     for (int i = 0; i < DQ / 4; ++i) {
-      const f32x4 x = ok ? src[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 x = ok ? src[4 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
       qv[4 * i] = x[0];
       qv[4 * i + 1] = x[1];
       qv[4 * i + 2] = x[2];
       qv[4 * i + 3] = x[3];
     }
   }
-  const float* kbase = kbar + (int64_t)bh * a.nb * D + DQ * g;
+  const float* kbase = kbar + (int64_t)bh * a.nb * D + 4 * g;
   for (int cb = wave; cb * 16 < a.nb; cb += kMfmaWaves) {
     const int col = cb * 16 + l16;
     const bool ok = col < a.nb;
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(Vs
     float kv[DQ];
 #pragma unroll
     for (int i = 0; i < DQ / 4; ++i) {
-      const f32x4 x = ok ? src[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 x = ok ? src[4 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
       kv[4 * i] = x[0];
       kv[4 * i + 1] = x[1];
       kv[4 * i + 2] = x[2];
@@ -402,7 +410,8 @@ hipError_t launch_mfma_kpl(const VsaArgs& a, const float* qbar, const float* kba
     raised.store(1, std::memory_order_release);
   }
   const int groups = (a.nq + kMfmaRows - 1) / kMfmaRows;
-  hipLaunchKernelGGL((vsa_score_topk_mfma_kernel<D, KPL>), dim3(groups * a.B * a.Hh), dim3(kMfmaWaves * 64), lds,
+  const int nwg = groups * a.B * a.Hh;
+  hipLaunchKernelGGL((vsa_score_topk_mfma_kernel<D, KPL>), dim3((nwg + 7) / 8 * 8), dim3(kMfmaWaves * 64), lds,
                      stream, a, qbar, kbar, sel);
   return hipGetLastError();
 }
