@@ -235,7 +235,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const VsaGrid& gk = a.gk;     // key/value side
   // [4][V_k] row offsets of the compact slots of a key cube, by extent type
   int32_t* stab = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);
-  int32_t* ssel = stab + 4 * gk.V;  // [topk] kept cubes, when a.sel_lds
+  // [topk] kept cubes as (first row, n | extent type << 16), when a.sel_lds
+  u32x2* ssel = reinterpret_cast<u32x2*>(stab + 4 * gk.V);
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
   // id is remapped to give each XCD a contiguous range of (head, block) work.
@@ -270,10 +271,12 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   }
   const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
   const bool sel_lds = a.sel_lds != 0;
-  if (sel_lds) {
+  if (sel_lds) {  // the walker's block descriptors, computed once here
     for (int i = tid; i < a.topk; i += NW * 64) {
-      const int c = selrow[i];
-      ssel[i] = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
+      int c = selrow[i];
+      c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
+      const Blk d = describe_block(gk, gk.Pb + c, KT);
+      ssel[i] = u32x2{(uint32_t)d.base, (uint32_t)d.n | ((uint32_t)d.type << 16)};
     }
   }
   __syncthreads();
@@ -351,17 +354,30 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int rot = a.walk_conc > 0
                       ? (int)((int64_t)((blockIdx.x / 8) % (uint32_t)a.walk_conc) * a.topk / a.walk_conc)
                       : 0;
-  auto kept_block = [&](int i) -> int {
-    if (i < gk.Pb) return i;
+  // the i-th kept block (key-side fields)
+  auto kept_desc = [&](int i) -> Blk {
+    if (i < gk.Pb) return describe_block(gk, i, KT);
     int t = i - gk.Pb + rot;
     if (t >= a.topk) t -= a.topk;
-    if (sel_lds) return gk.Pb + __builtin_amdgcn_readfirstlane(ssel[t]);
+    if (sel_lds) {
+      const u32x2 e = ssel[t];
+      const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)e[1]);
+      Blk d;
+      d.base = __builtin_amdgcn_readfirstlane((int)e[0]);
+      d.n = (int32_t)(w & 0xFFFFu);
+      d.type = (int32_t)(w >> 16);
+      d.ntiles = (d.n + KT - 1) / KT;
+      d.ew = d.ehw = 0;
+      d.mw = d.mhw = 0;
+      d.prefix = false;
+      return d;
+    }
     int c = selrow[t];
     c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
-    return gk.Pb + c;
+    return describe_block(gk, gk.Pb + c, KT);
   };
   int ibi = 0, ikt = 0;
-  Blk kd = describe_block(gk, kept_block(0), KT);
+  Blk kd = kept_desc(0);
   const uint32_t last_row = (uint32_t)(gk.P + gk.T * gk.H * gk.W - 1);  // bound of every k/v load row
 
   // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
@@ -402,7 +418,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     if (ikt >= kd.ntiles) {
       ikt = 0;
       ++ibi;
-      if (ibi < nkept) kd = describe_block(gk, kept_block(ibi), KT);
+      if (ibi < nkept) kd = kept_desc(ibi);
     }
     return m;
   };
@@ -444,7 +460,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       if (ikt >= kd.ntiles) {
         ikt = 0;
         ++ibi;
-        if (ibi < nkept) kd = describe_block(gk, kept_block(ibi), KT);
+        if (ibi < nkept) kd = kept_desc(ibi);
       }
     }
   };
@@ -870,8 +886,8 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
                   hipStream_t stream) {
   // K and V stages, the four slot tables, and the kept list when it fits
   const size_t lds_base = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.gk.V * 16;
-  const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS && lds_base + (size_t)a.topk * 4 <= 160 * 1024;
-  const size_t lds = lds_base + (sel_lds ? (size_t)a.topk * 4 : 0);
+  const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS && lds_base + (size_t)a.topk * 8 <= 160 * 1024;
+  const size_t lds = lds_base + (sel_lds ? (size_t)a.topk * 8 : 0);
   if (lds > 65536) {
     static bool raised = false;  // benign race: the attribute call is idempotent
     if (!raised) {
