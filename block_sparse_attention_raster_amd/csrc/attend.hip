@@ -15,18 +15,21 @@
 // block tokens are rows p*V + k. Both query rows and key tiles walk this
 // compact numbering, so a block of n tokens fills floor(n/KT) whole key
 // tiles and at most one tail tile. A tail tile's slots past n load the
-// block's first row for K and a zero row for V, so they need no masking: a
+// block's first row for K and zeros for V, so they need no masking: a
 // correction after the step removes them from the row sum. The row offset
 // (tt*H + hh)*W + ww of slot k depends only on the extents, which take four
 // values per grid (whole or tail along h and along w), so the workgroup
-// tabulates the four maps of the key grid at start-up and each load reads
-// its row offset from LDS; query rows (read once) unravel k with
-// multiply-high divisions. Query blocks follow q's grid and cube shape, key
+// tabulates the four maps of the key grid (and the linear one of prefix
+// blocks) at start-up as byte offsets, and each load reads its offset from
+// LDS; query rows (read once) unravel k with multiply-high divisions. Query blocks follow q's grid and cube shape, key
 // blocks k's (the two differ when q and k/v lie on different grids:
 // fastbsa package page, section "Use").
 //
 // Data movement. K and V tiles go from HBM straight into LDS with 16-byte
-// global_load_lds (no registers) into two rings of NSTAGE tiles each. Step s
+// copies that bypass registers (global_load_lds for K; buffer_load ... lds
+// for V, through a buffer resource whose byte range ends at the head's
+// last row, so that the out-of-range offset given to tail slots reads
+// zeros) into two rings of NSTAGE tiles each. Step s
 // reads K of tile s and V of tile s-1, so the copies of a tile's V are
 // issued one step after its K: step s issues K of tile s+NSTAGE-1 and V of
 // tile s+NSTAGE-2, each into the stage the previous step finished with.
@@ -65,6 +68,7 @@ namespace {
 
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -133,10 +137,6 @@ __device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
   return (int32_t)(((uint64_t)(uint32_t)x * m) >> 32);
 }
 
-// A zero value row: the tail slots of a key tile load their V rows from it
-// (in the pipelined kernel), so their P.V terms vanish without masking.
-__device__ __align__(256) __bf16 vsa_zero_row[128];
-
 // Valid region of a kept or query block.
 struct Blk {
   int32_t base;     // first token row (the row of index 0)
@@ -144,7 +144,7 @@ struct Blk {
   int32_t ntiles;   // key tiles of the compact numbering
   int32_t ew, ehw;  // valid extents ew and eh*ew (query rows unravel with them)
   uint64_t mw, mhw; // and their division magics
-  int32_t type;     // video cubes: 2*[eh is the tail] + [ew is the tail]
+  int32_t type;     // video cubes: 2*[eh is the tail] + [ew is the tail]; prefix blocks 4
   bool prefix;
 };
 
@@ -159,7 +159,7 @@ __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int
     d.ew = n;
     d.ehw = n;
     d.mw = d.mhw = 0;
-    d.type = 0;
+    d.type = 4;
     d.prefix = true;
     return d;
   }
@@ -192,9 +192,15 @@ __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
-__device__ __forceinline__ void dma16(const void* addr, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
+// The same through a buffer resource: a lane whose offset is past the
+// resource's byte range (num_records) gets zeros, and no memory is read.
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
+
+// Byte offset that is out of range of every V buffer resource (the plan
+// keeps a head's K/V byte span at or below it).
+constexpr uint32_t kOutOfRange = 0xFFFFFFC0u;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)((const __attribute__((address_space(3))) unsigned char*)p);
@@ -233,10 +239,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   unsigned char* kst = smem;                              // [NSTAGE][TILE_BYTES]
   unsigned char* vst = smem + NSTAGE * TILE_BYTES;        // [NSTAGE][TILE_BYTES]
   const VsaGrid& gk = a.gk;     // key/value side
-  // [4][V_k] row offsets of the compact slots of a key cube, by extent type
-  int32_t* stab = reinterpret_cast<int32_t*>(smem + 2 * NSTAGE * TILE_BYTES);
-  // [topk] kept cubes as (first row, n | extent type << 16), when a.sel_lds
-  u32x2* ssel = reinterpret_cast<u32x2*>(stab + 4 * gk.V);
+  // [5][V_k] byte offsets from a key block's first row of its compact
+  // slots: video cubes by extent type (0..3), prefix blocks (4)
+  uint32_t* stab = reinterpret_cast<uint32_t*>(smem + 2 * NSTAGE * TILE_BYTES);
+  // [topk] kept cubes as (first row's byte offset, n | extent type << 16),
+  // when a.sel_lds
+  u32x2* ssel = reinterpret_cast<u32x2*>(stab + 5 * gk.V);
+  const uint32_t rowb = (uint32_t)a.ksn * 2u;   // bytes between key rows
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
   // id is remapped to give each XCD a contiguous range of (head, block) work.
@@ -255,18 +264,23 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   if (slot0 >= qd.n) return;
 
   const int tid = threadIdx.x;
-  {  // Row offsets from a key cube's first row of its compact slots s, for
-     // the four extent types (eh, ew) in {ch, tail} x {cw, tail}: slot s is
-     // (tt, hh, ww) in raster order over the valid extents. Entries past a
-     // cube's token count are never used for a valid slot.
+  {  // Byte offsets from a key block's first row of its compact slots s:
+     // for the four cube extent types (eh, ew) in {ch, tail} x {cw, tail},
+     // slot s is (tt, hh, ww) in raster order over the valid extents; prefix
+     // blocks are contiguous. Entries past a block's token count are never
+     // used for a valid slot.
     const int tail_h = gk.H - (gk.nH - 1) * gk.ch, tail_w = gk.W - (gk.nW - 1) * gk.cw;
-    for (int idx = tid; idx < 4 * gk.V; idx += NW * 64) {
+    for (int idx = tid; idx < 5 * gk.V; idx += NW * 64) {
       const int t = idx / gk.V, s = idx - t * gk.V;
-      const int eh = (t >> 1) ? tail_h : gk.ch, ew = (t & 1) ? tail_w : gk.cw;
-      const int ehw = eh * ew;
-      const int tt = s / ehw, r = s - tt * ehw;
-      const int hh = r / ew, ww = r - hh * ew;
-      stab[idx] = (tt * gk.H + hh) * gk.W + ww;
+      int row = s;
+      if (t < 4) {
+        const int eh = (t >> 1) ? tail_h : gk.ch, ew = (t & 1) ? tail_w : gk.cw;
+        const int ehw = eh * ew;
+        const int tt = s / ehw, r = s - tt * ehw;
+        const int hh = r / ew, ww = r - hh * ew;
+        row = (tt * gk.H + hh) * gk.W + ww;
+      }
+      stab[idx] = (uint32_t)row * rowb;
     }
   }
   const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
@@ -276,7 +290,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       int c = selrow[i];
       c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
       const Blk d = describe_block(gk, gk.Pb + c, KT);
-      ssel[i] = u32x2{(uint32_t)d.base, (uint32_t)d.n | ((uint32_t)d.type << 16)};
+      ssel[i] = u32x2{(uint32_t)d.base * rowb, (uint32_t)d.n | ((uint32_t)d.type << 16)};
     }
   }
   __syncthreads();
@@ -290,10 +304,10 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // token row of compact index k < d.n of key block d
-  auto compact_row = [&](const Blk& d, int k) -> int {
-    if (d.prefix) return d.base + k;
-    return d.base + stab[d.type * gk.V + min(k, gk.V - 1)];
+  // byte offset from the head's first key row of compact index k < d.n of
+  // key block d (whose base the walker keeps in bytes)
+  auto compact_off = [&](const Blk& d, int k) -> uint32_t {
+    return (uint32_t)d.base + stab[d.type * gk.V + min(k, gk.V - 1)];
   };
   // token row of compact index k < d.n of the query block (q's grid; every
   // video cube, whole or partial, carries its extents' division magics)
@@ -355,8 +369,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
                       ? (int)((int64_t)((blockIdx.x / 8) % (uint32_t)a.walk_conc) * a.topk / a.walk_conc)
                       : 0;
   // the i-th kept block (key-side fields)
+  // (key side: base holds the first row's byte offset)
   auto kept_desc = [&](int i) -> Blk {
-    if (i < gk.Pb) return describe_block(gk, i, KT);
+    if (i < gk.Pb) {
+      Blk d = describe_block(gk, i, KT);
+      d.base = (int32_t)((uint32_t)d.base * rowb);
+      return d;
+    }
     int t = i - gk.Pb + rot;
     if (t >= a.topk) t -= a.topk;
     if (sel_lds) {
@@ -374,11 +393,24 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     }
     int c = selrow[t];
     c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
-    return describe_block(gk, gk.Pb + c, KT);
+    Blk d = describe_block(gk, gk.Pb + c, KT);
+    d.base = (int32_t)((uint32_t)d.base * rowb);
+    return d;
   };
   int ibi = 0, ikt = 0;
   Blk kd = kept_desc(0);
-  const uint32_t last_row = (uint32_t)(gk.P + gk.T * gk.H * gk.W - 1);  // bound of every k/v load row
+  // bound of every K load's row offset, and the V buffer resource: V of
+  // this head, num_records = its byte span, so that offsets at or past it
+  // (tail slots) read as zeros
+  const uint32_t last_b = (uint32_t)(gk.P + gk.T * gk.H * gk.W - 1) * rowb;
+  i32x4 vrsrc;
+  {
+    const uint64_t vb = (uint64_t)reinterpret_cast<uintptr_t>(vh);
+    vrsrc[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)vb);
+    vrsrc[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((vb >> 32) & 0xFFFFu));
+    vrsrc[2] = __builtin_amdgcn_readfirstlane((int32_t)(last_b + (uint32_t)D * 2u));
+    vrsrc[3] = 0x00020000;
+  }
 
   // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
   // for s = wave*SPW + j: key row (s*64 + lane)/CPR, chunk position
@@ -392,7 +424,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // vpend, and fire_v issues them one step later (V of a tile is first read
   // one step after its K). Returns the tile's validity mask (bit i: slot i
   // is valid), then advances the walker.
-  const unsigned char* vpend[SPW];
+  uint32_t vpend[SPW];
   auto issue_k = [&](int stage) -> uint64_t {
     const int t = ikt;
     unsigned char* kdst = kst + stage * TILE_BYTES;
@@ -406,12 +438,10 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       const int key = p / CPR, cp = p % CPR;
       const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
       const bool valid = key < nleft;
-      const int row = valid ? compact_row(kd, t * KT + key) : kd.base;
-      const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.ksn * 2u;
+      const uint32_t ro = valid ? compact_off(kd, t * KT + key) : (uint32_t)kd.base;
       const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
-      dma16(kh, ro + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
-      vpend[j] = valid ? reinterpret_cast<const unsigned char*>(vh) + ro + vo
-                       : reinterpret_cast<const unsigned char*>(vsa_zero_row) + vo;
+      dma16(kh, min(ro, last_b) + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
+      vpend[j] = valid ? ro + vo : kOutOfRange;
     }
     const uint64_t m = nleft >= KT ? FULLM : __ballot(lane < nleft);
     ++ikt;
@@ -424,35 +454,33 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   };
   auto fire_v = [&](int stage, int j) {
     const int s = wave * SPW + j;
-    dma16(vpend[j], lds_addr(vst + stage * TILE_BYTES + s * 1024));
+    dma16_buf(vrsrc, vpend[j], lds_addr(vst + stage * TILE_BYTES + s * 1024));
   };
 
   // Pipelined kernel: the walker describes the next tile in scalar
   // registers outside the compute step (branches, block descriptors), and
   // the step itself forms the per-lane load addresses (branch-free vector
-  // work, spread over its MFMA slots) and issues the copies. A video cube's
-  // slot rows come from the slot table of its extent type (one LDS read per
-  // load, issued several slots before the address is formed).
+  // work, spread over its MFMA slots) and issues the copies. A block's slot
+  // offsets come from the slot table of its type (one LDS read per load,
+  // issued several slots before the address is formed).
   struct Spec {
-    int32_t base;    // first token row of the block
-    int32_t nleft;   // valid slots from this tile on (KT or more: all)
+    uint32_t base;   // byte offset of the block's first row
+    int32_t nleft;   // valid slots from this tile on (KT or more: all; 0 past the walk)
     int32_t k0;      // compact index of the tile's first slot
-    int32_t tbase;   // video cubes: first slot-table entry of its type
-    int32_t mode;    // 1 prefix, 2 video cube, 3 nothing left
+    int32_t tbase;   // first slot-table entry of the block's type
   };
   struct Pend {
-    uint32_t ko[SPW];              // K byte offsets from kh
-    const unsigned char* va[SPW];  // V source addresses (zero row for tail slots)
+    uint32_t ko[SPW];  // K byte offsets from kh
+    uint32_t vo[SPW];  // V byte offsets from vh (out of range for tail slots)
   };
   // describes the walker's current tile as ring slot AHEAD, then advances
   auto spec = [&](Spec& sp, uint64_t& m, bool& e) {
     const bool any = ibi < nkept;
     const int t = ikt;
-    sp.base = any ? kd.base : 0;
-    sp.nleft = any ? kd.n - t * KT : KT;
+    sp.base = any ? (uint32_t)kd.base : 0u;
+    sp.nleft = any ? kd.n - t * KT : 0;
     sp.k0 = t * KT;
     sp.tbase = kd.type * gk.V;
-    sp.mode = !any ? 3 : kd.prefix ? 1 : 2;
     e = any;
     m = sp.nleft >= KT ? FULLM : ((1ull << sp.nleft) - 1ull);
     if (any) {
@@ -465,11 +493,9 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     }
   };
   // Per-thread constants of load j (16-byte unit (wave*SPW + j)*64 + lane
-  // of a tile): its key slot, the swizzled chunk offsets in K and V, and the
-  // zero row's address for tail slots.
+  // of a tile): its key slot and the swizzled chunk offsets in K and V.
   int keyj[SPW];
   uint32_t kcst[SPW], vcst[SPW];
-  const unsigned char* zvj[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int p = (wave * SPW + j) * 64 + lane;
@@ -478,35 +504,24 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     keyj[j] = key;
     kcst[j] = (uint32_t)((cp ^ (key & KSWZ)) * 16);
     vcst[j] = (uint32_t)((cp ^ fv) * 16);
-    zvj[j] = reinterpret_cast<const unsigned char*>(vsa_zero_row) + vcst[j];
   }
   // slot-table entry of this thread's load j of the tile `sp` describes
   // (clamped into the table: slots past the block's end are not used)
-  auto trow = [&](const Spec& sp, int j) -> int {
+  auto trow = [&](const Spec& sp, int j) -> uint32_t {
     return stab[sp.tbase + min(sp.k0 + keyj[j], gk.V - 1)];
   };
   // per-lane addresses of this thread's load j of the tile `sp` describes,
   // from its slot-table entry toff
-  auto addrs = [&](const Spec& sp, Pend& pd, int j, int toff) {
-    const int key = keyj[j];
-    const bool valid = key < sp.nleft;
-    const int kc = sp.k0 + key;
-    // blend the row formulas with opaque masks: a select on a uniform
-    // condition would become a branch and split the fenced step (and the
-    // per-lane validity likewise: a divergent branch). Past the walker's
-    // last tile (mode 3) the block is stale: row 0.
-    int m_pre = -(int)(sp.mode == 1), m_val = -(int)valid, m_none = -(int)(sp.mode == 3);
-    asm volatile("" : "+v"(m_pre), "+v"(m_val), "+v"(m_none));
-    int row = sp.base + ((toff & ~m_pre) | (kc & m_pre));
-    row = (row & m_val) | (sp.base & ~m_val);
-    row &= ~m_none;
-    // guard: never address past the last token row
-    const uint32_t ro = min((uint32_t)row, last_row) * (uint32_t)a.ksn * 2u;
-    pd.ko[j] = ro + kcst[j];
-    const uint64_t vv = (uint64_t)reinterpret_cast<uintptr_t>(vh) + (ro + vcst[j]);
-    const uint64_t vz = (uint64_t)reinterpret_cast<uintptr_t>(zvj[j]);
-    const uint64_t mv64 = (uint64_t)(int64_t)m_val;
-    pd.va[j] = reinterpret_cast<const unsigned char*>((vv & mv64) | (vz & ~mv64));
+  auto addrs = [&](const Spec& sp, Pend& pd, int j, uint32_t toff) {
+    // tail slots: K of the block's first row, V out of range (zeros);
+    // past the walk (nleft 0) every slot is a tail slot of row 0. The
+    // validity is an opaque mask: a select on it could become a divergent
+    // branch and split the fenced step.
+    int m_val = -(int)(keyj[j] < sp.nleft);
+    asm volatile("" : "+v"(m_val));
+    const uint32_t ro = sp.base + (toff & (uint32_t)m_val);
+    pd.ko[j] = min(ro, last_b) + kcst[j];   // guard: never past the last key row
+    pd.vo[j] = ((ro + vcst[j]) & (uint32_t)m_val) | (kOutOfRange & ~(uint32_t)m_val);
   };
   // load j of a refill: V of tile s + AHEAD - 1 (addresses from the step
   // before) into vstage, then K of tile s + AHEAD into kstage, whose V
@@ -515,7 +530,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     const int s = wave * SPW + j;
     fire_v(vstage, j);
     dma16(kh, pd.ko[j], lds_addr(kst + kstage * TILE_BYTES + s * 1024));
-    vpend[j] = pd.va[j];
+    vpend[j] = pd.vo[j];
   };
 
   // per-lane LDS offsets of the MFMA operands
@@ -884,8 +899,8 @@ int resident_per_xcd(const void* func, int threads, size_t lds) {
 template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
-  // K and V stages, the four slot tables, and the kept list when it fits
-  const size_t lds_base = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.gk.V * 16;
+  // K and V stages, the five slot tables, and the kept list when it fits
+  const size_t lds_base = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.gk.V * 20;
   const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS && lds_base + (size_t)a.topk * 8 <= 160 * 1024;
   const size_t lds = lds_base + (sel_lds ? (size_t)a.topk * 8 : 0);
   if (lds > 65536) {

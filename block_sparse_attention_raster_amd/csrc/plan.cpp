@@ -25,6 +25,9 @@ namespace {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Largest (N_k - 1) * kv_stride_n + head_dim: 2^32 - 64 bytes.
+constexpr int64_t kKvSpanElems = 0x7FFFFFE0;
+
 bool aligned16_elems(int64_t stride_elems) { return (stride_elems * 2) % 16 == 0; }
 
 // Largest element offset touched for a [B][Hh][N][D] view with these strides.
@@ -125,6 +128,10 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   if ((st = check_view(B, Hh, q.N, D, p.stride_b, p.stride_h, p.stride_n)) != VSA_OK) return st;
   if ((st = check_view(B, Hh, q.N, D, p.o_stride_b, p.o_stride_h, p.o_stride_n)) != VSA_OK) return st;
   if ((st = check_view(B, Hh, k.N, D, p.kv_stride_b, p.kv_stride_h, p.kv_stride_n)) != VSA_OK) return st;
+  // k/v rows are addressed by byte offsets from the head's first row, and
+  // offsets from 2^32 - 64 up mark tail slots: a head's k/v byte span stays
+  // below that
+  if ((k.N - 1) * p.kv_stride_n + D > kKvSpanElems) return VSA_ERR_OVERFLOW;
   // output rows must not overlap (each token row is written by one lane pair)
   if (p.o_stride_n < D) return VSA_ERR_INVALID_ARG;
 

@@ -28,7 +28,10 @@
  *                unless kv_stride_* are given; o has its own. Base pointers
  *                and strides*2 must be multiples of 16 bytes. With a key
  *                grid of its own, k and v hold N_k = P + T_k*H_k*W_k rows
- *                in raster order of that grid.
+ *                in raster order of that grid. Within one (b, h):
+ *                (N-1)*stride_n + head_dim <= 2^31 - 1 for q and o, and
+ *                (N_k-1)*kv_stride_n + head_dim <= 2^31 - 32 for k and v,
+ *                else VSA_ERR_OVERFLOW.
  *   workspace    float32 pooled means, written by vsa_select:
  *                  qbar [B][Hh][num_q_blocks][head_dim], then
  *                  kbar [B][Hh][num_blocks][head_dim] at byte offset

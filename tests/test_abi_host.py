@@ -123,6 +123,9 @@ def _status(**kw):
     (dict(strides=(1 << 40, 1 << 33, 1 << 23)), _lib.VSA_ERR_OVERFLOW),
     (dict(strides=(1 << 62, 1 << 33, 1 << 20), batch=4), _lib.VSA_ERR_OVERFLOW),
     (dict(strides=(0, 128, 128)), _lib.VSA_ERR_INVALID_ARG),
+    # one head's k/v span: (N - 1) * stride_n + D <= 2^31 - 32 elements
+    (dict(latent=(1, 1, 2), cube=(1, 1, 1), topk=1, strides=(1 << 33, 1 << 32, 0x7FFFFF60)), _lib.VSA_OK),
+    (dict(latent=(1, 1, 2), cube=(1, 1, 1), topk=1, strides=(1 << 33, 1 << 32, 0x7FFFFF68)), _lib.VSA_ERR_OVERFLOW),
 ])
 def test_plan_status_codes(kw, status):
     assert _status(**kw) == status
