@@ -93,13 +93,6 @@ struct Elem {
   static __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  // acc + both elements of a packed pair
-  static __device__ __forceinline__ float add2(uint32_t p, float acc) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), ones, acc, false);
-  }
-  // the high element of a packed pair as a float
-  static __device__ __forceinline__ float hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
 };
 template <>
 struct Elem<true> {
@@ -110,11 +103,6 @@ struct Elem<true> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                   0, 0);
   }
-  static __device__ __forceinline__ float add2(uint32_t p, float acc) {
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, acc, false);
-  }
-  static __device__ __forceinline__ float hi(uint32_t p) { return (float)__builtin_bit_cast(f16x2, p)[1]; }
 };
 
 // The values of x held by lanes l % 32 and 32 + l % 32 (the two halves of a
@@ -597,13 +585,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // the P.V MFMAs of tile `vs_` (P of the previous step in pb) with the next
   // block's V reads and, between them, the softmax of the new scores in
   // small pieces (row max, exponent offset, then pairs of exponentials
-  // packed to bf16). WITH_PV false (the first tile) keeps the slots without
+  // packed to bf16 for P.V; the row sum adds the fp32 exponentials). WITH_PV
+  // false (the first tile) keeps the slots without
   // their P.V work. Tail tiles need no masking here: their key slots past
   // the block's end repeat the block's first row, whose score the running
   // max has already seen (or sees in this tile), and their V rows are zero;
   // `tail_sum` then removes those slots from the row sum.
   auto step = [&](auto with_pv, int ks, int vs_, const bf16x8 (&pb)[QB][NKB][2], bf16x8 (&pn)[QB][NKB][2],
-                  float (&alpha)[QB], const Spec& sp, int kstage, int vstage) {
+                  float (&alpha)[QB], float& plast, const Spec& sp, int kstage, int vstage) {
     constexpr bool WITH_PV = decltype(with_pv)::value;
     static_assert(QB == 1, "the fixed schedule is written for one query block per wave");
     constexpr int KA = 6;                   // K reads ahead of their MFMA
@@ -691,9 +680,11 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       for (int k = 0; k < NPAIR; ++k) {
         if (p == P_PAIR0 + (k * (NP - P_PAIR0)) / NPAIR) {
           const int pkb = k / 8, phh = (k % 8) / 4, i = k % 4, r = 8 * phh + 2 * i;
-          const uint32_t w = E::pack2(__builtin_amdgcn_exp2f(fmaf(sa[pkb][r], cexp, -mc)),
-                                         __builtin_amdgcn_exp2f(fmaf(sa[pkb][r + 1], cexp, -mc)));
-          psum = E::add2(w, psum);
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[pkb][r], cexp, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sa[pkb][r + 1], cexp, -mc));
+          const uint32_t w = E::pack2(e0, e1);
+          psum += e0 + e1;
+          if (k == NPAIR - 1) plast = e1;
           u32x4 t = __builtin_bit_cast(u32x4, pn[0][pkb][phh]);
           t[i] = w;
           pn[0][pkb][phh] = __builtin_bit_cast(bf16x8, t);
@@ -706,15 +697,12 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 
   // Row-sum correction of a tail tile after `step`: a lane's slots past the
   // block's end all hold the score of the block's first row, so they added
-  // the same bf16 P, which the lane's last slot (key 32(NKB-1) + 28 + 4g + 3,
-  // always among them when the lane has any) carries in the high half of
-  // its last packed word.
-  auto tail_sum = [&](uint64_t cmask, const bf16x8 (&pn)[QB][NKB][2]) {
+  // the same p to the row sum; `plast` is p of the lane's last slot (key
+  // 32(NKB-1) + 28 + 4g + 3), always among them when the lane has any.
+  auto tail_sum = [&](uint64_t cmask, float plast) {
     const uint64_t mine = g ? 0xF0F0F0F0F0F0F0F0ull : 0x0F0F0F0F0F0F0F0Full;
     const int ninv = __builtin_popcountll(~cmask & FULLM & mine);
-    const uint32_t last = __builtin_bit_cast(u32x4, pn[0][NKB - 1][1])[3];
-    const float pbase = E::hi(last);
-    lrow[0] = fmaf(-(float)ninv, pbase, lrow[0]);
+    lrow[0] = fmaf(-(float)ninv, plast, lrow[0]);
   };
 
   // Publish: every wave has waited for its own loads of the tiles needed
@@ -805,8 +793,9 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       barrier();
       if constexpr (ACTIVE) {
         float alpha[QB];
-        step(F_{}, 0, 0, pb, pb, alpha, sp, AHEAD, AHEAD - 1);
-        if (mring[0] != FULLM) tail_sum(mring[0], pb);
+        float plast;
+        step(F_{}, 0, 0, pb, pb, alpha, plast, sp, AHEAD, AHEAD - 1);
+        if (mring[0] != FULLM) tail_sum(mring[0], plast);
         rescale(alpha);
       } else {
         fire_all(AHEAD, AHEAD - 1);
@@ -830,8 +819,9 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         if constexpr (ACTIVE) {
           bf16x8 pn[QB][NKB][2];
           float alpha[QB];
-          step(T_{}, cur, prev, pb, pn, alpha, sp, fst, vfst);
-          if (mring[0] != FULLM) tail_sum(mring[0], pn);
+          float plast;
+          step(T_{}, cur, prev, pb, pn, alpha, plast, sp, fst, vfst);
+          if (mring[0] != FULLM) tail_sum(mring[0], plast);
           rescale(alpha);
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {

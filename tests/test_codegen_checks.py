@@ -3,9 +3,8 @@ hipcc cross-compiles). They guard against silent failure modes:
 
 * register spills to scratch memory in the kernels (a reload's vmcnt wait
   would also wait for every global-to-LDS copy in flight);
-* row sums that read one packed P register several times (a bit_cast of a
-  vector element reads element 0);
-* global-to-LDS copies written as inline asm without their M0 set.
+* global-to-LDS and buffer-to-LDS copies written as inline asm without
+  their M0 set.
 """
 import os
 import re
@@ -45,30 +44,20 @@ def _blocks(asm):
     return out
 
 
-def test_row_sums_read_distinct_p_registers(tmp_path):
-    asm = _device_asm("attend.hip", tmp_path)
-    checked = 0
-    for blk in _blocks(asm):
-        srcs = [re.search(r"v_dot2c_f32_b?f16_e32 v\d+, \S+, (v\d+)", i).group(1) for i in blk
-                if re.match(r"v_dot2c_f32_b?f16", i)]
-        if len(srcs) >= 4:
-            assert len(set(srcs)) == len(srcs), srcs
-            checked += 1
-    assert checked > 0
-
-
 def test_lds_copies_set_m0(tmp_path):
     asm = _device_asm("attend.hip", tmp_path)
-    checked = 0
+    checked = {"global": 0, "buffer": 0}
     for blk in _blocks(asm):
         m0_set = False
         for i in blk:
             if re.match(r"s_\w+ m0,", i):
                 m0_set = True
-            if i.startswith("global_load_lds_dwordx4"):
-                assert m0_set, "global_load_lds without M0 set in its block"
-                checked += 1
-    assert checked > 0
+            kind = ("global" if i.startswith("global_load_lds_dwordx4") else
+                    "buffer" if re.match(r"buffer_load_dwordx4 .* lds$", i) else None)
+            if kind:
+                assert m0_set, f"{i}: LDS copy without M0 set in its block"
+                checked[kind] += 1
+    assert checked["global"] > 0 and checked["buffer"] > 0, checked
 
 
 @pytest.mark.parametrize("src", ["attend.hip", "select.hip", "pool.hip"])
