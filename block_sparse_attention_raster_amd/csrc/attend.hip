@@ -927,13 +927,14 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
 // Tilings, all on the pipelined step: cubes of up to 64 tokens use 2-wave
 // workgroups (64 query rows) with 32-key tiles in rings of two (32 KB of LDS
 // for D = 128, so four workgroups share a CU); larger cubes use 8-wave
-// workgroups (256 query rows) with 64-key tiles in rings of three.
+// workgroups (256 query rows) with 64-key tiles in rings of two (D = 128;
+// 1-3% faster than three, 3-6% at top-k 16) or three (D = 64).
 template <bool F16>
 static hipError_t dispatch(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                            const int32_t* sel, void* o, hipStream_t stream) {
   if (a.D == 128) {
     if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, F16>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, 3, 64, 2, F16>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 1, 2, 64, 2, F16>(a, q, k, v, sel, o, stream);
   }
   if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, F16>(a, q, k, v, sel, o, stream);
   return launch<64, 8, 1, 3, 64, 2, F16>(a, q, k, v, sel, o, stream);
