@@ -236,19 +236,32 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const uint32_t rowb = (uint32_t)a.ksn * 2u;   // bytes between key rows
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
-  // id is remapped to give each XCD a contiguous range of (head, block) work.
-  const int nwg = a.B * a.Hh * a.nq * a.tiles;
-  const int per_xcd = (nwg + 7) / 8;
-  const int lid = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (lid >= nwg) return;
-  int bid = lid;
+  // id is remapped to give each XCD a contiguous range of units (a unit is
+  // RW query slots of one query block of one (batch, head)). The last
+  // a.split_tail units of each range run as two workgroups of RW/2 slots
+  // each (the other waves only load tiles): dispatched last, they shorten
+  // the final, partly filled round of workgroups.
+  const int nunits = a.B * a.Hh * a.nq * a.tiles;
+  const int per_xcd = (nunits + 7) / 8;
+  const int xcd = (int)(blockIdx.x % 8), jx = (int)(blockIdx.x / 8);
+  const int nx = min(per_xcd, nunits - xcd * per_xcd);   // units of this XCD
+  const int sx = min(a.split_tail, max(nx, 0));          // of which split
+  int unit = xcd * per_xcd + jx, half = -1;              // half: -1 whole, else 0 or 1
+  if (jx >= nx - sx) {
+    const int hj = jx - (nx - sx);
+    if (hj >= 2 * sx) return;
+    unit = xcd * per_xcd + nx - sx + hj / 2;
+    half = hj % 2;
+  }
+  int bid = unit;
   const int tile = bid % a.tiles;
   bid /= a.tiles;
   const int qblk = bid % a.nq;
   const int bh = bid / a.nq;
   const int b = bh / a.Hh, h = bh - b * a.Hh;
   const Blk qd = describe_block(a.gq, qblk, KT);
-  const int slot0 = tile * RW;
+  const int slot0 = tile * RW + (half > 0 ? RW / 2 : 0);
+  const int rows_here = half < 0 ? RW : RW / 2;   // query slots of this workgroup
   if (slot0 >= qd.n) return;
 
   const int tid = threadIdx.x;
@@ -313,8 +326,9 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   bf16x8 qreg[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int slot = slot0 + wave * 32 * QB + qb * 32 + l32;
-    qrow[qb] = slot < qd.n ? query_row(qd, slot) : -1;
+    const int rel = wave * 32 * QB + qb * 32;
+    const int slot = slot0 + rel + l32;
+    qrow[qb] = slot < qd.n && rel < rows_here ? query_row(qd, slot) : -1;
     if (qrow[qb] >= 0) {
       const __bf16* src = qh + (int64_t)qrow[qb] * a.sn + 8 * g;
 #pragma unroll
@@ -906,17 +920,20 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   VsaArgs b = a;
   constexpr int RW = NW * 32 * QB;  // query slots per workgroup
   b.tiles = (a.gq.V + RW - 1) / RW;
-  const int64_t nwg = (int64_t)a.B * a.Hh * a.nq * b.tiles;
-  if (nwg > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((nwg + 7) / 8 * 8));
+  const int64_t nunits = (int64_t)a.B * a.Hh * a.nq * b.tiles;
+  if (nunits > (int64_t)INT32_MAX / 2 - 64) return hipErrorInvalidValue;
+  const int conc = resident_per_xcd(
+      reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), NW * 64, lds);
+  if (conc <= 0) return hipErrorInvalidValue;
   b.sel_lds = sel_lds;
-  b.walk_conc = 0;
-  if (NW == 2) {  // small-cube kernel: stagger the walks of the resident set
-    const int conc = resident_per_xcd(
-        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), NW * 64, lds);
-    if (conc < 0) return hipErrorInvalidValue;
-    b.walk_conc = conc;
-  }
+  b.walk_conc = NW == 2 ? conc : 0;   // small-cube kernel: stagger the walks of the resident set
+  // Large-cube kernel: when the last round of workgroups on each XCD is at
+  // most half full, its units run as half-row workgroups (twice as many,
+  // each quicker: one wave per SIMD instead of two).
+  const int64_t per_xcd = (nunits + 7) / 8;
+  const int64_t rem = per_xcd % conc;
+  b.split_tail = (NW == 8 && rem > 0 && 2 * rem <= conc) ? (int32_t)rem : 0;
+  dim3 grid((unsigned)(8 * (per_xcd + b.split_tail)));
   hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), grid, dim3(NW * 64), lds, stream, b,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();

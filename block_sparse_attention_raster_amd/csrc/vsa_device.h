@@ -59,6 +59,8 @@ struct VsaArgs {
   int32_t sel_lds;       // attention: the kept-cube list is copied to LDS
   int32_t walk_conc;     // attention workgroups resident per XCD whose walks
                          // are phase-staggered (0: no stagger)
+  int32_t split_tail;    // attention: units at the end of each XCD's range
+                         // that run as two half-row workgroups (0: none)
 };
 
 // Valid region of one block: first token row, extents of the (tt, hh, ww)
