@@ -417,15 +417,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
   // for s = wave*SPW + j: key row (s*64 + lane)/CPR, chunk position
   // (s*64 + lane)%CPR, XOR-swizzled by key (K: chunk ^ (key & KSWZ); V: see
-  // the transposed reads). The per-lane offsets are recomputed at every
-  // issue from an opaque copy of the lane id, so that they are not kept in
-  // registers across the compute steps.
-  // Issues the loads of the walker's current tile into `stage` and returns
-  // its validity mask (bit i: slot i of the tile is valid); then advances.
-  // K of the walker's current tile into `stage` now; its V addresses go to
-  // vpend, and fire_v issues them one step later (V of a tile is first read
-  // one step after its K). Returns the tile's validity mask (bit i: slot i
-  // is valid), then advances the walker.
+  // the transposed reads).
+  // issue_k (prologue): K of the walker's current tile into `stage` now;
+  // its V offsets go to vpend, and fire_v issues them one step later (V of
+  // a tile is first read one step after its K). Returns the tile's
+  // validity mask (bit i: slot i is valid), then advances the walker. The
+  // per-lane offsets come from an opaque copy of the lane id, so that they
+  // are not kept in registers across the compute steps.
   uint32_t vpend[SPW];
   auto issue_k = [&](int stage) -> uint64_t {
     const int t = ikt;
