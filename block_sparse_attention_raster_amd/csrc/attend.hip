@@ -906,14 +906,10 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS && lds_base + (size_t)a.topk * 8 <= 160 * 1024;
   const size_t lds = lds_base + (sel_lds ? (size_t)a.topk * 8 : 0);
   if (lds > 65536) {
-    static bool raised = false;  // benign race: the attribute call is idempotent
-    if (!raised) {
-      const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+    static std::atomic<uint64_t> raised{0};
+    const hipError_t e = vsa_raise_lds_limit(
+        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), raised);
+    if (e != hipSuccess) return e;
   }
   VsaArgs b = a;
   constexpr int RW = NW * 32 * QB;  // query slots per workgroup

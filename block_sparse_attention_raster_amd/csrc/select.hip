@@ -375,12 +375,10 @@ namespace {
 template <int D, int R>
 hipError_t launch_rows(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel, size_t lds,
                        hipStream_t stream) {
-  static std::atomic<int> raised{0};
-  if (lds > 65536 && !raised.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vsa_score_topk_kernel<D, R>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static std::atomic<uint64_t> raised{0};
+  if (lds > 65536) {
+    const hipError_t e = vsa_raise_lds_limit(reinterpret_cast<const void*>(&vsa_score_topk_kernel<D, R>), raised);
     if (e != hipSuccess) return e;
-    raised.store(1, std::memory_order_release);
   }
   const int groups = (a.nq + R - 1) / R;
   hipLaunchKernelGGL((vsa_score_topk_kernel<D, R>), dim3(groups * a.B * a.Hh), dim3(kSelThreads), lds, stream,
@@ -402,12 +400,11 @@ hipError_t launch_d(const VsaArgs& a, const float* qbar, const float* kbar, int3
 template <int D, int KPL>
 hipError_t launch_mfma_kpl(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel, size_t lds,
                            hipStream_t stream) {
-  static std::atomic<int> raised{0};
-  if (lds > 65536 && !raised.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vsa_score_topk_mfma_kernel<D, KPL>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static std::atomic<uint64_t> raised{0};
+  if (lds > 65536) {
+    const hipError_t e =
+        vsa_raise_lds_limit(reinterpret_cast<const void*>(&vsa_score_topk_mfma_kernel<D, KPL>), raised);
     if (e != hipSuccess) return e;
-    raised.store(1, std::memory_order_release);
   }
   const int groups = (a.nq + kMfmaRows - 1) / kMfmaRows;
   const int nwg = groups * a.B * a.Hh;
