@@ -493,3 +493,50 @@ def test_hip_graph_capture_and_replay():
         assert torch.equal(out, ref), f"replay {i}"
         assert torch.equal(sel, ref_sel), f"replay {i}"
         _ = (q.float() * 2).sum().item()      # eager work between replays
+
+
+_CAPTURE_FIRST = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import torch
+import block_sparse_attention_raster_amd as vsa
+from block_sparse_attention_raster_amd import synthetic
+w = synthetic.custom_workload("capture_first", seed=55, batch=1, heads=2, head_dim=128,
+                              latent=(5, 9, 17), cube=(4, 8, 8), topk=3, prefix_len=20)
+q, k, v = (synthetic.bits_to_torch(x, "cuda") for x in synthetic.make_inputs(w))
+pl = vsa.plan_for(q, w.latent, w.cube, 3, 20)
+ws = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device="cuda")
+sel = torch.empty((pl.batch, pl.heads, pl.num_q_blocks, pl.topk), dtype=torch.int32, device="cuda")
+out = torch.empty_like(q)
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):   # the first library calls of this process
+    vsa.select(pl, q, k, ws, sel)
+    vsa.attend(pl, q, k, v, sel, out)
+outs = []
+for _ in range(3):
+    out.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    outs.append(out.clone())
+sel2, _ = vsa.select(pl, q, k)
+ref = vsa.attend(pl, q, k, v, sel2)
+torch.cuda.synchronize()
+assert torch.equal(sel, sel2)
+assert all(torch.equal(o, ref) for o in outs)
+print("capture-first ok", flush=True)
+"""
+
+
+def test_hip_graph_capture_as_first_call():
+    """A process whose first library calls happen under HIP graph capture
+    (the launchers' one-time set-up, such as the LDS limit and occupancy
+    queries, then runs inside the capture) replays to the eager result."""
+    import os
+    import subprocess
+    _announce("HIP graph capture as the first call (child process)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, root], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0 and "capture-first ok" in r.stdout, (r.returncode, r.stdout[-2000:], r.stderr[-4000:])
