@@ -66,11 +66,9 @@
 
 namespace {
 
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -127,7 +125,8 @@ __device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
 
 // Valid region of a kept or query block.
 struct Blk {
-  int32_t base;     // first token row (the row of index 0)
+  int32_t base;     // first token row (the row of index 0); in the key walker,
+                    // that row's byte offset from the head's first row
   int32_t n;        // valid tokens
   int32_t ntiles;   // key tiles of the compact numbering
   int32_t ew, ehw;  // valid extents ew and eh*ew (query rows unravel with them)
