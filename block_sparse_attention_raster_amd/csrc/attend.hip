@@ -29,12 +29,13 @@
 // copies that bypass registers (global_load_lds for K; buffer_load ... lds
 // for V, through a buffer resource whose byte range ends at the head's
 // last row, so that the out-of-range offset given to tail slots reads
-// zeros) into two rings of NSTAGE tiles each. Step s
-// reads K of tile s and V of tile s-1, so the copies of a tile's V are
-// issued one step after its K: step s issues K of tile s+NSTAGE-1 and V of
-// tile s+NSTAGE-2, each into the stage the previous step finished with.
-// Each wave issues its share, waits for its own copies of what the next
-// step reads, and one barrier per tile publishes them.
+// zeros) into two rings of NSTAGE tiles each. Step s reads K of tile s and
+// V of tile s-1, so the copies of a tile's V are issued one step after its
+// K: step s issues K of tile s+A and V of tile s+A-1, A = NSTAGE - BSTEP,
+// into stages whose reads all finished before the last barrier. Each wave
+// issues its share and waits for its own copies, and a barrier before every
+// BSTEP-th step publishes them (BSTEP 2: one barrier per two tiles, with
+// copies two tiles ahead in rings of four).
 // Both tiles keep the natural [key][head_dim] order with the 16-byte chunks
 // of each key row XOR-swizzled (applied on the global side, since the LDS
 // position of each lane's 16 bytes is fixed by its lane id).
@@ -200,7 +201,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16, int BSTEP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
                                                              const __bf16* __restrict__ k,
@@ -727,7 +728,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
 
   // Tile ring: slot i holds the i-th tile from the one the next step starts
   // with. AHEAD tiles are in flight when a step begins.
-  constexpr int AHEAD = NSTAGE - 1;
+  constexpr int AHEAD = NSTAGE - BSTEP;
+  static_assert(BSTEP == 1 || (BSTEP == 2 && NSTAGE % 2 == 0 && AHEAD >= 2), "barrier spacing");
   uint64_t mring[AHEAD + 1];
   bool ering[AHEAD + 1];
 #pragma unroll
@@ -782,9 +784,10 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       // Software pipeline. Tile t sits in stage t % NSTAGE. Step j runs QK
       // of tile j and the P.V of tile j-1 (whose P the previous step made),
       // with the softmax of tile j on the vector ALUs while the P.V matrix
-      // ops run. Barrier j publishes tile j; every wave has then finished
-      // step j-1, so tile j-2's stage is free, and step j issues the copies
-      // of tile j + NSTAGE - 2 into it (prepared before the barrier).
+      // ops run. The barrier before every BSTEP-th step publishes what the
+      // next BSTEP steps read; every wave has then finished the steps before
+      // it, so the stages they read are free, and step j copies K of tile
+      // j + AHEAD and V of tile j + AHEAD - 1 into them.
       bf16x8 pb[QB][NKB][2];
       Spec sp;
       auto fire_all = [&](int kstage, int vstage) {
@@ -800,7 +803,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       };
       // first tile: QK and softmax only (every kept list has a tile)
       spec(sp, mring[AHEAD], ering[AHEAD]);
-      wait_first();
+      if constexpr (BSTEP == 1) wait_first(); else wait_vmcnt<0>();
       barrier();
       if constexpr (ACTIVE) {
         float alpha[QB];
@@ -821,8 +824,13 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         const int vfst = fst == 0 ? NSTAGE - 1 : fst - 1;                               // V refill
         if (have) spec(sp, mring[AHEAD], ering[AHEAD]);
         // the last P.V reads V of the last tile, copied one step after its K
-        if (have) wait_first(); else wait_vmcnt<0>();
-        barrier();
+        if constexpr (BSTEP == 1) {
+          if (have) wait_first(); else wait_vmcnt<0>();
+          barrier();
+        } else if ((cur & 1) == 0 || !have) {  // every other step, and before the last P.V
+          wait_vmcnt<0>();
+          barrier();
+        }
         if (!have) {
           if constexpr (ACTIVE) pv(prev, pb);
           break;
@@ -897,7 +905,7 @@ int resident_per_xcd(const void* func, int threads, size_t lds) {
   return conc;
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16>
+template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16, int BSTEP>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
   // K and V stages, the five slot tables, and the kept list when it fits
@@ -907,7 +915,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   if (lds > 65536) {
     static std::atomic<uint64_t> raised{0};
     const hipError_t e = vsa_raise_lds_limit(
-        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), raised);
+        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16, BSTEP>), raised);
     if (e != hipSuccess) return e;
   }
   VsaArgs b = a;
@@ -916,7 +924,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   const int64_t nunits = (int64_t)a.B * a.Hh * a.nq * b.tiles;
   if (nunits > (int64_t)INT32_MAX / 2 - 64) return hipErrorInvalidValue;
   const int conc = resident_per_xcd(
-      reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), NW * 64, lds);
+      reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16, BSTEP>), NW * 64, lds);
   if (conc <= 0) return hipErrorInvalidValue;
   b.sel_lds = sel_lds;
   b.walk_conc = NW == 2 ? conc : 0;   // small-cube kernel: stagger the walks of the resident set
@@ -927,7 +935,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   const int64_t rem = per_xcd % conc;
   b.split_tail = (NW == 8 && rem > 0 && 2 * rem <= conc) ? (int32_t)rem : 0;
   dim3 grid((unsigned)(8 * (per_xcd + b.split_tail)));
-  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16>), grid, dim3(NW * 64), lds, stream, b,
+  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16, BSTEP>), grid, dim3(NW * 64), lds, stream, b,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();
 }
@@ -936,18 +944,20 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
 
 // Tilings, all on the pipelined step: cubes of up to 64 tokens use 2-wave
 // workgroups (64 query rows) with 32-key tiles in rings of two (32 KB of LDS
-// for D = 128, so four workgroups share a CU); larger cubes use 8-wave
-// workgroups (256 query rows) with 64-key tiles in rings of two (D = 128;
-// 1-3% faster than three, 3-6% at top-k 16) or three (D = 64).
+// for D = 128, so four workgroups share a CU) and a barrier per tile; larger
+// cubes use 8-wave workgroups (256 query rows) with 64-key tiles, for
+// D = 128 in rings of four with one barrier per two tiles (128 KB; 1-2%
+// faster than rings of two with a barrier per tile), for D = 64 in rings of
+// three with a barrier per tile.
 template <bool F16>
 static hipError_t dispatch(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                            const int32_t* sel, void* o, hipStream_t stream) {
   if (a.D == 128) {
-    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, F16>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, 2, 64, 2, F16>(a, q, k, v, sel, o, stream);
+    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, F16, 1>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 1, 4, 64, 2, F16, 2>(a, q, k, v, sel, o, stream);
   }
-  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, F16>(a, q, k, v, sel, o, stream);
-  return launch<64, 8, 1, 3, 64, 2, F16>(a, q, k, v, sel, o, stream);
+  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, F16, 1>(a, q, k, v, sel, o, stream);
+  return launch<64, 8, 1, 3, 64, 2, F16, 1>(a, q, k, v, sel, o, stream);
 }
 
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
