@@ -84,6 +84,9 @@ SMALL = [
     # a cube volume between the tilings (330 tokens: two query tiles) with
     # partial prefix and cubes
     ("cube_v330", 1, 2, 64, (7, 12, 13), (3, 10, 11), 2, 17),
+    # 36 query blocks over 8 XCD ranges of 5: the last range holds one unit,
+    # every unit runs as two half-row workgroups
+    ("units_uneven_xcd", 1, 3, 128, (9, 10, 11), (4, 8, 8), 5, 0),
 ]
 
 
@@ -305,6 +308,11 @@ def test_workload_wan_f16():
 def test_workload_long720p():
     w = synthetic.WORKLOADS["long720p"]
     _full_check(w, 60, heads=[(0, 0), (0, 31)], blocks_per_head=12)
+
+
+def test_workload_long720p_f16():
+    w = synthetic.WORKLOADS["long720p"]
+    _full_check(w, 60, heads=[(0, 0), (0, 31)], blocks_per_head=12, dtype="f16")
 
 
 def test_workload_prefix():
