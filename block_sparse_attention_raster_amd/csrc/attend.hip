@@ -3,10 +3,10 @@
 // blocks; section "Choose top-k": prefix blocks are always kept; section
 // "Verify routing and fallback": non-causal, scale head_size^-1/2).
 //
-// Work split. One workgroup owns RW = NW*32*QB query slots of one query block
-// of one (batch, head); each wave owns 32*QB of them. The kept key blocks
-// (all prefix blocks, then the selected cubes in ascending id order, cyclic
-// from a start chosen per workgroup) are walked in tiles of KT key slots.
+// Work split. One workgroup owns RW = NW*32 query slots of one query block
+// of one (batch, head); each wave owns 32 of them. The kept key blocks (all
+// prefix blocks, then the selected cubes in ascending id order, cyclic from
+// a start chosen per workgroup) are walked in tiles of KT key slots.
 //
 // Index map (fastbsa package page, section "How it works": the raster to
 // block map is evaluated inside the kernel). The n valid tokens of a block
@@ -21,9 +21,11 @@
 // values per grid (whole or tail along h and along w), so the workgroup
 // tabulates the four maps of the key grid (and the linear one of prefix
 // blocks) at start-up as byte offsets, and each load reads its offset from
-// LDS; query rows (read once) unravel k with multiply-high divisions. Query blocks follow q's grid and cube shape, key
-// blocks k's (the two differ when q and k/v lie on different grids:
-// fastbsa package page, section "Use").
+// LDS; query rows (read once) unravel k with multiply-high divisions. Query
+// blocks follow q's grid and cube shape, key blocks k's (the two differ when
+// q and k/v lie on different grids: fastbsa package page, section "Use").
+// The workgroup also describes its selected cubes once, in walk order, in an
+// LDS table, so moving from one kept block to the next costs one LDS read.
 //
 // Data movement. K and V tiles go from HBM straight into LDS with 16-byte
 // copies that bypass registers (global_load_lds for K; buffer_load ... lds
@@ -53,11 +55,20 @@
 // step; the matching V^T operand comes from two ds_read_b64_tr_b16 reads of
 // the [key][head_dim] tile: in each 16-lane group, lane i addresses row
 // key0 + i/4 at head-dim column base + 4*(i%4) and lane j receives the four
-// keys key0..key0+3 of column base + j. Every lane owns one query row: row max
-// and sum need one exchange between the lane halves and rescaling O is a
-// per-lane scalar. Softmax runs in base 2: p = 2^(s*c - m) with
-// c = head_dim^-1/2 * log2(e) and m a running bound of the scaled row max,
-// the same softmax.
+// keys key0..key0+3 of column base + j. Every lane owns one query row.
+//
+// Softmax in base 2 with a lazy offset: p = 2^x with x = c*s - m,
+// c = head_dim^-1/2 * log2(e). For bf16 inputs the Q rows in registers are
+// pre-multiplied by c (rounded once to bf16) and the first QK MFMA of each
+// key block starts its accumulator at -m instead of 0, so the MFMA yields x
+// and p = 2^x needs no further arithmetic. For fp16 inputs (held to a
+// tighter tolerance) x = fma(s, c, -m) in fp32 instead, with Q unscaled.
+// The offset m of a row is raised only when the
+// tile's sum of p leaves a bound (so no p can exceed it): then the tile is
+// redone with m raised to the row's maximum and O and l are rescaled. The
+// first tile always sets m to its row maximum. Both O and l carry the same
+// factor 2^-m, so this is the same softmax. The row sum adds p rounded to
+// the input type (as P.V uses them) with v_dot2 against (1, 1).
 
 #include <atomic>
 #include <type_traits>
@@ -73,12 +84,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two floats to packed bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
-}
-
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -88,20 +93,41 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <bool F16>
 struct Elem {
   // two floats to one packed pair (round to nearest even)
-  static __device__ __forceinline__ uint32_t pack2(float x, float y) { return pack_bf16x2(x, y); }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+  }
+  // the upper element of a packed pair, as float
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+  // acc + both elements of a packed pair
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                           acc, false);
+  }
   static __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // largest tile sum of p before the offset is raised (p <= this sum)
+  static constexpr float kSumLimit = 16777216.f;  // 2^24
+  // Q pre-scaled by c and the offset folded into the QK accumulators
+  static constexpr bool kPrescale = true;
 };
 template <>
 struct Elem<true> {
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
   }
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+  }
+  // the upper element of a packed pair, as float
+  static __device__ __forceinline__ float hi(uint32_t w) { return sum2(w & 0xFFFF0000u, 0.f); }
   static __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                   0, 0);
   }
+  // fp16 P must stay below 65504
+  static constexpr float kSumLimit = 32768.f;  // 2^15
+  static constexpr bool kPrescale = false;
 };
 
 // The values of x held by lanes l % 32 and 32 + l % 32 (the two halves of a
@@ -112,12 +138,12 @@ __device__ __forceinline__ f32x2 halves(float x) {
   return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-// Lazy rescaling of the running softmax state: the row max used in the
-// exponent is raised only when a tile's max exceeds it by more than this many
-// powers of two, so p = 2^(s*c - m) stays below 2^8 and the O / l rescale is
-// skipped on most tiles. The result is the same softmax (both O and l carry
-// the same factor).
-constexpr float kRescaleLog2 = 8.f;
+// Keeps x in a register at this point of the program (the compiler may not
+// move its computation past here, nor fold it into later uses).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
 
 // floor(x / d) for x, d < 2^16 with m = ceil(2^32 / d) (m = 2^32 for d = 1).
 __device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
@@ -126,24 +152,21 @@ __device__ __forceinline__ int32_t fast_div(int32_t x, uint64_t m) {
 
 // Valid region of a kept or query block.
 struct Blk {
-  int32_t base;     // first token row (the row of index 0); in the key walker,
-                    // that row's byte offset from the head's first row
+  int32_t base;     // first token row (the row of index 0)
   int32_t n;        // valid tokens
-  int32_t ntiles;   // key tiles of the compact numbering
   int32_t ew, ehw;  // valid extents ew and eh*ew (query rows unravel with them)
   uint64_t mw, mhw; // and their division magics
   int32_t type;     // video cubes: 2*[eh is the tail] + [ew is the tail]; prefix blocks 4
   bool prefix;
 };
 
-__device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int32_t kt) {
+__device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk) {
   Blk d;
   if (blk < g.Pb) {
     const int32_t s = blk * g.V;
     const int32_t n = min(g.V, g.P - s);
     d.base = s;
     d.n = n;
-    d.ntiles = (n + kt - 1) / kt;
     d.ew = n;
     d.ehw = n;
     d.mw = d.mhw = 0;
@@ -161,7 +184,6 @@ __device__ __forceinline__ Blk describe_block(const VsaGrid& g, int32_t blk, int
   const int ih = eh != g.ch, iw = ew != g.cw;
   d.base = g.P + (t0 * g.H + h0) * g.W + w0;
   d.n = et * eh * ew;
-  d.ntiles = (d.n + kt - 1) / kt;
   d.ew = ew;
   d.ehw = eh * ew;
   d.mw = g.magic_ew[iw];
@@ -201,19 +223,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16, int BSTEP>
+// LDS bytes of the slot tables: five maps of V_k entries plus KT entries of
+// padding (a tile's slots past its block's end read there; their offsets
+// are masked), rounded up to 16 bytes so that the kept-block table after
+// them is aligned.
+__host__ __device__ constexpr uint32_t slot_table_bytes(int32_t vk, int kt) {
+  return ((uint32_t)(5 * vk + kt) * 4u + 15u) & ~15u;
+}
+
+template <int D, int NW, int NSTAGE, int KT, int WPE, bool F16, int BSTEP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
-void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
-                                                             const __bf16* __restrict__ k,
-                                                             const __bf16* __restrict__ v,
-                                                             const int32_t* __restrict__ sel,
-                                                             __bf16* __restrict__ o) {
+void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                       const __bf16* __restrict__ v, const int32_t* __restrict__ sel, __bf16* __restrict__ o) {
   using E = Elem<F16>;
   constexpr int CPR = D / 8;             // 16-byte chunks per key row
   constexpr int NKB = KT / 32;           // 32-key MFMA blocks per tile
   constexpr uint64_t FULLM = KT == 64 ? ~0ull : ((1ull << (KT & 63)) - 1ull);
   static_assert(KT == 32 || KT == 64, "key tile of 32 or 64 slots");
-  constexpr int RW = NW * 32 * QB;       // query slots per workgroup
+  constexpr int RW = NW * 32;            // query slots per workgroup
   constexpr int UNITS = KT * CPR;        // 16-byte units per K (or V) tile
   constexpr int SLABS = UNITS / 64;      // wave-wide loads per tensor per tile
   constexpr int SPW = SLABS / NW;        // of which each wave issues
@@ -227,12 +254,12 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   unsigned char* kst = smem;                              // [NSTAGE][TILE_BYTES]
   unsigned char* vst = smem + NSTAGE * TILE_BYTES;        // [NSTAGE][TILE_BYTES]
   const VsaGrid& gk = a.gk;     // key/value side
-  // [5][V_k] byte offsets from a key block's first row of its compact
-  // slots: video cubes by extent type (0..3), prefix blocks (4)
+  // [5][V_k] (+ padding) byte offsets from a key block's first row of its
+  // compact slots: video cubes by extent type (0..3), prefix blocks (4)
   uint32_t* stab = reinterpret_cast<uint32_t*>(smem + 2 * NSTAGE * TILE_BYTES);
-  // [topk] kept cubes as (first row's byte offset, n | extent type << 16),
-  // when a.sel_lds
-  u32x2* ssel = reinterpret_cast<u32x2*>(stab + 5 * gk.V);
+  // [topk] selected cubes in walk order, as (first row's byte offset,
+  // n | slot-table base << 16)
+  u32x2* blist = reinterpret_cast<u32x2*>(smem + 2 * NSTAGE * TILE_BYTES + slot_table_bytes(gk.V, KT));
   const uint32_t rowb = (uint32_t)a.ksn * 2u;   // bytes between key rows
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
@@ -259,10 +286,22 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int qblk = bid % a.nq;
   const int bh = bid / a.nq;
   const int b = bh / a.Hh, h = bh - b * a.Hh;
-  const Blk qd = describe_block(a.gq, qblk, KT);
+  const Blk qd = describe_block(a.gq, qblk);
   const int slot0 = tile * RW + (half > 0 ? RW / 2 : 0);
   const int rows_here = half < 0 ? RW : RW / 2;   // query slots of this workgroup
   if (slot0 >= qd.n) return;
+
+  // Walk phase. The selected cubes are visited in ascending id order from a
+  // starting position rot, cyclically. With many small workgroups resident
+  // per XCD, a workgroup starts whenever an earlier one ends, so in steady
+  // state the resident set started at staggered times; a start position
+  // proportional to the dispatch index within the resident set keeps the
+  // cubes being read at any moment within a narrow band of cube ids, which
+  // the XCD's L2 then holds. The order only changes float rounding, and it
+  // depends on the launch alone, so results stay reproducible.
+  const int rot = a.walk_conc > 0
+                      ? (int)((int64_t)((blockIdx.x / 8) % (uint32_t)a.walk_conc) * a.topk / a.walk_conc)
+                      : 0;
 
   const int tid = threadIdx.x;
   {  // Byte offsets from a key block's first row of its compact slots s:
@@ -271,7 +310,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
      // blocks are contiguous. Entries past a block's token count are never
      // used for a valid slot.
     const int tail_h = gk.H - (gk.nH - 1) * gk.ch, tail_w = gk.W - (gk.nW - 1) * gk.cw;
-    for (int idx = tid; idx < 5 * gk.V; idx += NW * 64) {
+    for (int idx = tid; idx < 5 * gk.V + KT; idx += NW * 64) {
       const int t = idx / gk.V, s = idx - t * gk.V;
       int row = s;
       if (t < 4) {
@@ -281,17 +320,18 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         const int hh = r / ew, ww = r - hh * ew;
         row = (tt * gk.H + hh) * gk.W + ww;
       }
-      stab[idx] = (uint32_t)row * rowb;
+      stab[idx] = t < 5 ? (uint32_t)row * rowb : 0u;
     }
-  }
-  const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
-  const bool sel_lds = a.sel_lds != 0;
-  if (sel_lds) {  // the walker's block descriptors, computed once here
+    // the selected cubes in walk order (ids clamped into range: other
+    // contents of sel stay in bounds)
+    const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
     for (int i = tid; i < a.topk; i += NW * 64) {
-      int c = selrow[i];
+      int t = i + rot;
+      if (t >= a.topk) t -= a.topk;
+      int c = selrow[t];
       c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
-      const Blk d = describe_block(gk, gk.Pb + c, KT);
-      ssel[i] = u32x2{(uint32_t)d.base * rowb, (uint32_t)d.n | ((uint32_t)d.type << 16)};
+      const Blk d = describe_block(gk, gk.Pb + c);
+      blist[i] = u32x2{(uint32_t)d.base * rowb, (uint32_t)d.n | ((uint32_t)(d.type * gk.V) << 16)};
     }
   }
   __syncthreads();
@@ -305,102 +345,82 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // byte offset from the head's first key row of compact index k < d.n of
-  // key block d (whose base the walker keeps in bytes)
-  auto compact_off = [&](const Blk& d, int k) -> uint32_t {
-    return (uint32_t)d.base + stab[d.type * gk.V + min(k, gk.V - 1)];
-  };
   // token row of compact index k < d.n of the query block (q's grid; every
   // video cube, whole or partial, carries its extents' division magics)
-  auto query_row = [&](const Blk& d, int k) -> int {
-    if (d.prefix) return d.base + k;
-    const int tt = fast_div(k, d.mhw);
-    const int r = k - tt * d.ehw;
+  auto query_row = [&](const Blk& d, int kk) -> int {
+    if (d.prefix) return d.base + kk;
+    const int tt = fast_div(kk, d.mhw);
+    const int r = kk - tt * d.ehw;
     const int hh = fast_div(r, d.mw);
     const int ww = r - hh * d.ew;
     return d.base + (tt * a.gq.H + hh) * a.gq.W + ww;
   };
 
-  // ---- Q rows of this wave, in MFMA B-operand layout
-  int qrow[QB];
-  bf16x8 qreg[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int rel = wave * 32 * QB + qb * 32;
+  // ---- Q row of this lane in MFMA B-operand layout (for bf16 scaled by
+  // c = head_dim^-1/2 log2(e))
+  const float cexp = a.scale_log2e;
+  int qrow;
+  bf16x8 qreg[D / 16];
+  {
+    const int rel = wave * 32;
     const int slot = slot0 + rel + l32;
-    qrow[qb] = slot < qd.n && rel < rows_here ? query_row(qd, slot) : -1;
-    if (qrow[qb] >= 0) {
-      const __bf16* src = qh + (int64_t)qrow[qb] * a.sn + 8 * g;
+    qrow = slot < qd.n && rel < rows_here ? query_row(qd, slot) : -1;
+    if (qrow >= 0) {
+      const __bf16* src = qh + (int64_t)qrow * a.sn + 8 * g;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) qreg[qb][c] = *reinterpret_cast<const bf16x8*>(src + 16 * c);
+      for (int c = 0; c < D / 16; ++c) qreg[c] = *reinterpret_cast<const bf16x8*>(src + 16 * c);
     } else {
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) qreg[qb][c] = bf16x8{};
+      for (int c = 0; c < D / 16; ++c) qreg[c] = bf16x8{};
     }
   }
   // Q must be resident before the tile loads start: inside the loop the
   // compiler cannot count how many later loads follow it and would otherwise
   // wait for all of them before every tile.
   wait_vmcnt<0>();
-  bool wave_active = false;
+  if constexpr (E::kPrescale) {
+    static_assert(!F16, "the pre-scaled Q rows are bf16");
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) wave_active |= qrow[qb] >= 0;
-  wave_active = __ballot(wave_active) != 0;
-
-  f32x16 oacc[QB][D / 32];
-  float mrow[QB], lrow[QB];
+    for (int c = 0; c < D / 16; ++c) {
+      u32x4 w = __builtin_bit_cast(u32x4, qreg[c]);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    mrow[qb] = -INFINITY;
-    lrow[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
+      for (int i = 0; i < 4; ++i)
+        w[i] = E::pack2(__uint_as_float(w[i] << 16) * cexp, __uint_as_float(w[i] & 0xFFFF0000u) * cexp);
+      qreg[c] = __builtin_bit_cast(bf16x8, w);
+    }
   }
+  const bool wave_active = __ballot(qrow >= 0) != 0;
 
-  // ---- kept-block walk (issue side)
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float lrow = 0.f;               // this lane's part of the row sum l
+  float mneg = 0.f;               // -m (both lanes of a row agree)
+  f32x16 negm = {};               // -m in every entry: with kPrescale the QK accumulators start there
+
+  // ---- kept-block walk (issue side): all prefix blocks of the key grid,
+  // then the selected cubes from the LDS table
   const int nkept = gk.Pb + a.topk;
-  // Walk phase. The selected cubes are visited in ascending id order from a
-  // starting position rot, cyclically. With many small workgroups resident
-  // per XCD, a workgroup starts whenever an earlier one ends, so in steady
-  // state the resident set started at staggered times; a start position
-  // proportional to the dispatch index within the resident set keeps the
-  // cubes being read at any moment within a narrow band of cube ids, which
-  // the XCD's L2 then holds. The order only changes float rounding, and it
-  // depends on the launch alone, so results stay reproducible.
-  const int rot = a.walk_conc > 0
-                      ? (int)((int64_t)((blockIdx.x / 8) % (uint32_t)a.walk_conc) * a.topk / a.walk_conc)
-                      : 0;
-  // the i-th kept block (key-side fields)
-  // (key side: base holds the first row's byte offset)
-  auto kept_desc = [&](int i) -> Blk {
+  int ibi = 0;        // current kept block
+  int kt0 = 0;        // compact index of its next tile's first slot
+  uint32_t kbase = 0; // its first row's byte offset
+  int kn = 0;         // its valid tokens
+  int ktab = 0;       // its slot-table base (extent type * V_k)
+  auto load_block = [&](int i) {
     if (i < gk.Pb) {
-      Blk d = describe_block(gk, i, KT);
-      d.base = (int32_t)((uint32_t)d.base * rowb);
-      return d;
-    }
-    int t = i - gk.Pb + rot;
-    if (t >= a.topk) t -= a.topk;
-    if (sel_lds) {
-      const u32x2 e = ssel[t];
+      const int s = i * gk.V;
+      kbase = (uint32_t)s * rowb;
+      kn = min(gk.V, gk.P - s);
+      ktab = 4 * gk.V;
+    } else {
+      const u32x2 e = blist[i - gk.Pb];
+      kbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)e[0]);
       const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)e[1]);
-      Blk d;
-      d.base = __builtin_amdgcn_readfirstlane((int)e[0]);
-      d.n = (int32_t)(w & 0xFFFFu);
-      d.type = (int32_t)(w >> 16);
-      d.ntiles = (d.n + KT - 1) / KT;
-      d.ew = d.ehw = 0;
-      d.mw = d.mhw = 0;
-      d.prefix = false;
-      return d;
+      kn = (int)(w & 0xFFFFu);
+      ktab = (int)(w >> 16);
     }
-    int c = selrow[t];
-    c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
-    Blk d = describe_block(gk, gk.Pb + c, KT);
-    d.base = (int32_t)((uint32_t)d.base * rowb);
-    return d;
   };
-  int ibi = 0, ikt = 0;
-  Blk kd = kept_desc(0);
+  load_block(0);
   // bound of every K load's row offset, and the V buffer resource: V of
   // this head, num_records = its byte span, so that offsets at or past it
   // (tail slots) read as zeros
@@ -414,86 +434,41 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     vrsrc[3] = 0x00020000;
   }
 
-  // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
-  // for s = wave*SPW + j: key row (s*64 + lane)/CPR, chunk position
-  // (s*64 + lane)%CPR, XOR-swizzled by key (K: chunk ^ (key & KSWZ); V: see
-  // the transposed reads).
-  // issue_k (prologue): K of the walker's current tile into `stage` now;
-  // its V offsets go to vpend, and fire_v issues them one step later (V of
-  // a tile is first read one step after its K). Returns the tile's
-  // validity mask (bit i: slot i is valid), then advances the walker. The
-  // per-lane offsets come from an opaque copy of the lane id, so that they
-  // are not kept in registers across the compute steps.
-  uint32_t vpend[SPW];
-  auto issue_k = [&](int stage) -> uint64_t {
-    const int t = ikt;
-    unsigned char* kdst = kst + stage * TILE_BYTES;
-    const int nleft = kd.n - t * KT;          // valid slots from this tile on
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int s = wave * SPW + j;
-      const int p = s * 64 + ln;
-      const int key = p / CPR, cp = p % CPR;
-      const int fv = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-      const bool valid = key < nleft;
-      const uint32_t ro = valid ? compact_off(kd, t * KT + key) : (uint32_t)kd.base;
-      const uint32_t vo = (uint32_t)((cp ^ fv) * 16);
-      dma16(kh, min(ro, last_b) + (uint32_t)((cp ^ (key & KSWZ)) * 16), lds_addr(kdst + s * 1024));
-      vpend[j] = valid ? ro + vo : kOutOfRange;
-    }
-    const uint64_t m = nleft >= KT ? FULLM : __ballot(lane < nleft);
-    ++ikt;
-    if (ikt >= kd.ntiles) {
-      ikt = 0;
-      ++ibi;
-      if (ibi < nkept) kd = kept_desc(ibi);
-    }
-    return m;
-  };
-  auto fire_v = [&](int stage, int j) {
-    const int s = wave * SPW + j;
-    dma16_buf(vrsrc, vpend[j], lds_addr(vst + stage * TILE_BYTES + s * 1024));
-  };
-
-  // Pipelined kernel: the walker describes the next tile in scalar
-  // registers outside the compute step (branches, block descriptors), and
-  // the step itself forms the per-lane load addresses (branch-free vector
-  // work, spread over its MFMA slots) and issues the copies. A block's slot
-  // offsets come from the slot table of its type (one LDS read per load,
-  // issued several slots before the address is formed).
+  // One tile of the walk: the block's first row, the valid slots from the
+  // tile on (KT or more: all; 0 past the walk) and the slot-table index of
+  // its first slot.
   struct Spec {
-    uint32_t base;   // byte offset of the block's first row
-    int32_t nleft;   // valid slots from this tile on (KT or more: all; 0 past the walk)
-    int32_t k0;      // compact index of the tile's first slot
-    int32_t tbase;   // first slot-table entry of the block's type
+    uint32_t base;
+    int32_t nleft;
+    int32_t tk0;
   };
   struct Pend {
     uint32_t ko[SPW];  // K byte offsets from kh
     uint32_t vo[SPW];  // V byte offsets from vh (out of range for tail slots)
   };
-  // describes the walker's current tile as ring slot AHEAD, then advances
+  // describes the walker's current tile, then advances
   auto spec = [&](Spec& sp, uint64_t& m, bool& e) {
     const bool any = ibi < nkept;
-    const int t = ikt;
-    sp.base = any ? (uint32_t)kd.base : 0u;
-    sp.nleft = any ? kd.n - t * KT : 0;
-    sp.k0 = t * KT;
-    sp.tbase = kd.type * gk.V;
+    sp.base = any ? kbase : 0u;
+    sp.nleft = any ? kn - kt0 : 0;
+    sp.tk0 = ktab + kt0;
     e = any;
     m = sp.nleft >= KT ? FULLM : ((1ull << sp.nleft) - 1ull);
     if (any) {
-      ++ikt;
-      if (ikt >= kd.ntiles) {
-        ikt = 0;
+      if (sp.nleft > KT) {
+        kt0 += KT;
+      } else {
+        kt0 = 0;
         ++ibi;
-        if (ibi < nkept) kd = kept_desc(ibi);
+        if (ibi < nkept) load_block(ibi);
       }
     }
   };
-  // Per-thread constants of load j (16-byte unit (wave*SPW + j)*64 + lane
-  // of a tile): its key slot and the swizzled chunk offsets in K and V.
+
+  // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
+  // for s = wave*SPW + j: key row (s*64 + lane)/CPR, chunk position
+  // (s*64 + lane)%CPR, XOR-swizzled by key (K: chunk ^ (key & KSWZ); V: see
+  // the transposed reads).
   int keyj[SPW];
   uint32_t kcst[SPW], vcst[SPW];
 #pragma unroll
@@ -506,10 +481,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     vcst[j] = (uint32_t)((cp ^ fv) * 16);
   }
   // slot-table entry of this thread's load j of the tile `sp` describes
-  // (clamped into the table: slots past the block's end are not used)
-  auto trow = [&](const Spec& sp, int j) -> uint32_t {
-    return stab[sp.tbase + min(sp.k0 + keyj[j], gk.V - 1)];
-  };
+  // (past the block's end it reads the next map or the padding: masked)
+  auto trow = [&](const Spec& sp, int j) -> uint32_t { return stab[sp.tk0 + keyj[j]]; };
   // per-lane addresses of this thread's load j of the tile `sp` describes,
   // from its slot-table entry toff
   auto addrs = [&](const Spec& sp, Pend& pd, int j, uint32_t toff) {
@@ -523,6 +496,12 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     pd.ko[j] = min(ro, last_b) + kcst[j];   // guard: never past the last key row
     pd.vo[j] = ((ro + vcst[j]) & (uint32_t)m_val) | (kOutOfRange & ~(uint32_t)m_val);
   };
+  // V copies wait one step after their K copies
+  uint32_t vpend[SPW];
+  auto fire_v = [&](int stage, int j) {
+    const int s = wave * SPW + j;
+    dma16_buf(vrsrc, vpend[j], lds_addr(vst + stage * TILE_BYTES + s * 1024));
+  };
   // load j of a refill: V of tile s + AHEAD - 1 (addresses from the step
   // before) into vstage, then K of tile s + AHEAD into kstage, whose V
   // addresses replace the ones just used
@@ -531,6 +510,18 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     fire_v(vstage, j);
     dma16(kh, pd.ko[j], lds_addr(kst + kstage * TILE_BYTES + s * 1024));
     vpend[j] = pd.vo[j];
+  };
+  // K of the tile `sp` describes into `stage` now, V addresses kept for
+  // fire_v (the prologue)
+  auto issue_k = [&](const Spec& sp, int stage) {
+    Pend pd;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      addrs(sp, pd, j, trow(sp, j));
+      const int s = wave * SPW + j;
+      dma16(kh, pd.ko[j], lds_addr(kst + stage * TILE_BYTES + s * 1024));
+      vpend[j] = pd.vo[j];
+    }
   };
 
   // per-lane LDS offsets of the MFMA operands
@@ -541,7 +532,6 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   const int vhalf = (i16 & 1) * 8;
   const int vfv = (D == 128) ? 4 * (vrow & 3) : 4 * ((vrow >> 1) & 1);
 
-  const float cexp = a.scale_log2e;
   constexpr int NC = D / 16;       // 16-wide head-dim steps of S^T = K Q^T
   constexpr int NVR = 4 * NKB;     // transposed reads per 32-wide head-dim block of P.V
 
@@ -560,7 +550,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   };
 
   // O^T += V^T P^T for the tile in `stage`, one head-dim block of 32 at a time
-  auto pv = [&](int stage, const bf16x8 (&pb)[QB][NKB][2]) {
+  auto pv = [&](int stage, const bf16x8 (&pb)[NKB][2]) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       u32x2 vr[NVR];
@@ -572,51 +562,89 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         for (int hh = 0; hh < 2; ++hh) {
           const u32x4 w = {vr[4 * kb + 2 * hh][0], vr[4 * kb + 2 * hh][1], vr[4 * kb + 2 * hh + 1][0],
                            vr[4 * kb + 2 * hh + 1][1]};
-          const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = E::mfma(vop, pb[qb][kb][hh], oacc[qb][db]);
+          oacc[db] = E::mfma(__builtin_bit_cast(bf16x8, w), pb[kb][hh], oacc[db]);
         }
     }
   };
 
-  auto rescale = [&](const float (&alpha)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (__ballot(alpha[qb] != 1.f) != 0) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha[qb];
-      }
-    }
+  // x of register r of key block kb of the QK accumulators
+  auto xval = [&](const f32x16 (&sa)[NKB], int kb, int r) -> float {
+    if constexpr (E::kPrescale) return sa[kb][r];
+    else return fmaf(sa[kb][r], cexp, mneg);
+  };
+  // p = 2^x of score pair k of this lane (registers r, r+1 of key block
+  // pkb), packed into the P operand pn; the pair's sum goes to ps[k % 4].
+  // A lane's pairs k = 8*pkb + 4*phh + i cover keys 32*pkb + 16*phh + 8*(i/2)
+  // + 4g + 2*(i%2) + {0, 1}.
+  constexpr int NPAIR = NKB * 8;
+  auto soft_pair = [&](int kk, const f32x16 (&sa)[NKB], bf16x8 (&pn)[NKB][2], float (&ps)[4]) {
+    const int pkb = kk / 8, phh = (kk % 8) / 4, i = kk % 4, r = 8 * phh + 2 * i;
+    const float e0 = __builtin_amdgcn_exp2f(xval(sa, pkb, r));
+    const float e1 = __builtin_amdgcn_exp2f(xval(sa, pkb, r + 1));
+    uint32_t w = E::pack2(e0, e1);
+    pin(w);
+    ps[kk % 4] = E::sum2(w, ps[kk % 4]);
+    pin(ps[kk % 4]);
+    u32x4 t = __builtin_bit_cast(u32x4, pn[pkb][phh]);
+    t[i] = w;
+    pn[pkb][phh] = __builtin_bit_cast(bf16x8, t);
   };
 
-  // One pipelined step, QB == 1, in a fixed issue order of 32 (D = 128) or
-  // 16 (D = 64) slots of one MFMA each, fenced so that the compiler keeps
-  // the order: first the QK MFMAs of tile `ks` with the K reads KA slots
-  // ahead and, in the last slots, the first head-dim block's V reads; then
-  // the P.V MFMAs of tile `vs_` (P of the previous step in pb) with the next
-  // block's V reads and, between them, the softmax of the new scores in
-  // small pieces (row max, exponent offset, then pairs of exponentials
-  // packed to bf16 for P.V; the row sum adds the fp32 exponentials). WITH_PV
-  // false (the first tile) keeps the slots without
-  // their P.V work. Tail tiles need no masking here: their key slots past
-  // the block's end repeat the block's first row, whose score the running
-  // max has already seen (or sees in this tile), and their V rows are zero;
-  // `tail_sum` then removes those slots from the row sum.
-  auto step = [&](auto with_pv, int ks, int vs_, const bf16x8 (&pb)[QB][NKB][2], bf16x8 (&pn)[QB][NKB][2],
-                  float (&alpha)[QB], float& plast, const Spec& sp, int kstage, int vstage) {
+  // The slow path of the softmax of one tile (the first tile, or a tile
+  // whose sum of p left the bound in some row): rows that need it (both
+  // lanes of a row decide together) raise m to their maximum x over the
+  // tile, the tile's p and sums are recomputed, and O and l of those rows
+  // are rescaled by 2^-delta. Returns the tile's sum of p of this lane.
+  auto raise_offset = [&](f32x16 (&sa)[NKB], bf16x8 (&pn)[NKB][2], bool need, bool first) -> float {
+    float mx = xval(sa, 0, 0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, xval(sa, kb, r));
+    const f32x2 hm = halves(mx);
+    const f32x2 hn = halves(need ? 1.f : 0.f);
+    const bool needr = first || hn[0] + hn[1] > 0.f;
+    const float delta = needr ? fmaxf(hm[0], hm[1]) : 0.f;
+    if constexpr (E::kPrescale) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sa[kb] -= delta;
+      negm -= delta;
+    }
+    mneg -= delta;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NPAIR; ++kk) soft_pair(kk, sa, pn, ps);
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      lrow *= alpha;
+    }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // One pipelined step, in a fixed issue order of 32 (D = 128) or 16
+  // (D = 64) slots of one MFMA each, fenced so that the compiler keeps the
+  // order: first the QK MFMAs of tile `ks` with the K reads KA slots ahead
+  // and, in the last slots, the first head-dim block's V reads; then the
+  // P.V MFMAs of tile `vs_` (P of the previous step in pb) with the next
+  // block's V reads and, between them, the exponentials of the new scores
+  // in pairs packed into pn, with their sums. WITH_PV false (the first tile)
+  // runs only the QK half; SOFT false leaves the exponentials out. Tail
+  // tiles need no masking here: their key slots past the block's end repeat
+  // the block's first row and their V rows are zero; `tail_sum` then
+  // removes those slots from the row sum.
+  auto step = [&](auto with_pv, auto soft, int ks, int vs_, const bf16x8 (&pb)[NKB][2], bf16x8 (&pn)[NKB][2],
+                  f32x16 (&sa)[NKB], float (&ps)[4], const Spec& sp, int kstage, int vstage) {
     constexpr bool WITH_PV = decltype(with_pv)::value;
-    static_assert(QB == 1, "the fixed schedule is written for one query block per wave");
+    constexpr bool SOFT = decltype(soft)::value;
     constexpr int KA = 6;                   // K reads ahead of their MFMA
     constexpr int NQ = NKB * NC;            // QK MFMAs
     constexpr int NDB = D / 32;             // head-dim blocks of P.V
     constexpr int PPD = 2 * NKB;            // P.V MFMAs per head-dim block
     constexpr int NP = NDB * PPD;           // P.V MFMAs
     constexpr int RPS = NVR / PPD;          // V reads per P.V slot (next block)
-    constexpr int NPAIR = NKB * 8;          // exponential pairs per lane
-    constexpr int P_M0 = 0, P_M1 = (NP >= 16 ? 2 : 1), P_M2 = P_M1 + 1, P_PAIR0 = P_M2 + 1;
-    static_assert(NVR % PPD == 0 && P_PAIR0 < NP, "schedule shape");
-    f32x16 sa[NKB];
+    static_assert(NVR % PPD == 0 && NPAIR % NP == 0, "schedule shape");
     bf16x8 kop[NQ];
     u32x2 vr[NDB][NVR];
     Pend pd;
@@ -628,27 +656,26 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
     constexpr bool SPREAD = 1 + 2 * (SPW - 1) < NQ / 2;
     auto rd_slot = [](int j) { return SPREAD ? 1 + 2 * j : (j * (NQ / 2)) / SPW; };
     auto fire_gap = [](int j) { return SPREAD ? 2 * j : (j * (NQ / 2)) / SPW; };
-    float mx = 0.f, mc = 0.f, psum = 0.f;
 #pragma unroll
     for (int i = 0; i < KA; ++i) kop[i] = kread(ks, i / NC, i % NC);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (q + KA < NQ) kop[q + KA] = kread(ks, (q + KA) / NC, (q + KA) % NC);
+    for (int qq = 0; qq < NQ; ++qq) {
+      if (qq + KA < NQ) kop[qq + KA] = kread(ks, (qq + KA) / NC, (qq + KA) % NC);
       // first block's V reads, two per slot in the last NVR/2 slots
-      if (WITH_PV && q >= NQ - NVR / 2) {
-        const int i = 2 * (q - (NQ - NVR / 2));
+      if (WITH_PV && qq >= NQ - NVR / 2) {
+        const int i = 2 * (qq - (NQ - NVR / 2));
         vr[0][i] = vread(vs_, 0, i);
         vr[0][i + 1] = vread(vs_, 0, i + 1);
       }
-      const int kb = q / NC, c = q % NC;
-      sa[kb] = E::mfma(kop[q], qreg[0][c], c == 0 ? f32x16{} : sa[kb]);
+      const int kb = qq / NC, c = qq % NC;
+      sa[kb] = E::mfma(kop[qq], qreg[c], c != 0 ? sa[kb] : E::kPrescale ? negm : f32x16{});
       // the refill of the stage freed by this step's barrier: slot-table
       // read of load j in slot 1 + 2j, its addresses and copies in slot
       // NQ/2 + 2j
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
-        if (q == rd_slot(j)) tv[j] = trow(sp, j);
-        if (q == NQ / 2 + fire_gap(j)) {
+        if (qq == rd_slot(j)) tv[j] = trow(sp, j);
+        if (qq == NQ / 2 + fire_gap(j)) {
           addrs(sp, pd, j, tv[j]);
           fire(pd, kstage, vstage, j);
         }
@@ -665,56 +692,28 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
         }
         const u32x4 w = {vr[db][4 * kb + 2 * hh][0], vr[db][4 * kb + 2 * hh][1], vr[db][4 * kb + 2 * hh + 1][0],
                          vr[db][4 * kb + 2 * hh + 1][1]};
-        oacc[0][db] =
-            E::mfma(__builtin_bit_cast(bf16x8, w), pb[0][kb][hh], oacc[0][db]);
+        oacc[db] = E::mfma(__builtin_bit_cast(bf16x8, w), pb[kb][hh], oacc[db]);
       }
-      // softmax pieces
-      if (p == P_M0) {
-        mx = sa[0][0];
+      if constexpr (SOFT) {
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[0][r]);
-      }
-      if (p == P_M1) {
-#pragma unroll
-        for (int k2 = 1; k2 < NKB; ++k2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[k2][r]);
-      }
-      if (p == P_M2) {
-        const f32x2 hv = halves(mx);
-        const float m = fmaxf(hv[0], hv[1]) * cexp;
-        const float mold = mrow[0];
-        mc = m > mold + kRescaleLog2 ? m : mold;
-        alpha[0] = __builtin_amdgcn_exp2f(mold - mc);
-        mrow[0] = mc;
-      }
-#pragma unroll
-      for (int k = 0; k < NPAIR; ++k) {
-        if (p == P_PAIR0 + (k * (NP - P_PAIR0)) / NPAIR) {
-          const int pkb = k / 8, phh = (k % 8) / 4, i = k % 4, r = 8 * phh + 2 * i;
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[pkb][r], cexp, -mc));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sa[pkb][r + 1], cexp, -mc));
-          const uint32_t w = E::pack2(e0, e1);
-          psum += e0 + e1;
-          if (k == NPAIR - 1) plast = e1;
-          u32x4 t = __builtin_bit_cast(u32x4, pn[0][pkb][phh]);
-          t[i] = w;
-          pn[0][pkb][phh] = __builtin_bit_cast(bf16x8, t);
-        }
+        for (int kk = p * (NPAIR / NP); kk < (p + 1) * (NPAIR / NP); ++kk) soft_pair(kk, sa, pn, ps);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lrow[0] = fmaf(lrow[0], alpha[0], psum);
   };
 
-  // Row-sum correction of a tail tile after `step`: a lane's slots past the
-  // block's end all hold the score of the block's first row, so they added
-  // the same p to the row sum; `plast` is p of the lane's last slot (key
-  // 32(NKB-1) + 28 + 4g + 3), always among them when the lane has any.
+  // Row-sum correction of a tail tile: a lane's slots past the block's end
+  // all hold the score of the block's first row, so they added the same p
+  // to the row sum; `plast` is p of the lane's last slot (key
+  // 32(NKB-1) + 24 + 4g + 3), always among them when the lane has any.
   auto tail_sum = [&](uint64_t cmask, float plast) {
     const uint64_t mine = g ? 0xF0F0F0F0F0F0F0F0ull : 0x0F0F0F0F0F0F0F0Full;
     const int ninv = __builtin_popcountll(~cmask & FULLM & mine);
-    lrow[0] = fmaf(-(float)ninv, plast, lrow[0]);
+    lrow = fmaf(-(float)ninv, plast, lrow);
+  };
+  // p of the lane's last slot, as the row sum added it
+  auto last_p = [&](const bf16x8 (&pn)[NKB][2]) -> float {
+    return E::hi(__builtin_bit_cast(u32x4, pn[NKB - 1][1])[3]);
   };
 
   // Publish: every wave has waited for its own loads of the tiles needed
@@ -746,8 +745,9 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
       for (int j = 0; j < SPW; ++j) fire_v(i - 1, j);
     }
     if (ibi < nkept) {
-      mring[i] = issue_k(i);
-      ering[i] = true;
+      Spec sp0;
+      spec(sp0, mring[i], ering[i]);
+      issue_k(sp0, i);
     }
   }
   // wait for this wave's copies of the K of ring slot 0 and of the V of the
@@ -780,80 +780,82 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   // accumulators in fixed registers.
   auto run = [&](auto active) {
     constexpr bool ACTIVE = decltype(active)::value;
-    {
-      // Software pipeline. Tile t sits in stage t % NSTAGE. Step j runs QK
-      // of tile j and the P.V of tile j-1 (whose P the previous step made),
-      // with the softmax of tile j on the vector ALUs while the P.V matrix
-      // ops run. The barrier before every BSTEP-th step publishes what the
-      // next BSTEP steps read; every wave has then finished the steps before
-      // it, so the stages they read are free, and step j copies K of tile
-      // j + AHEAD and V of tile j + AHEAD - 1 into them.
-      bf16x8 pb[QB][NKB][2];
-      Spec sp;
-      auto fire_all = [&](int kstage, int vstage) {
-        Pend pd;
-        int tv[SPW];
+    // Software pipeline. Tile t sits in stage t % NSTAGE. Step j runs QK
+    // of tile j and the P.V of tile j-1 (whose P the previous step made),
+    // with the exponentials of tile j on the vector ALUs while the P.V
+    // matrix ops run. The barrier before every BSTEP-th step publishes what
+    // the next BSTEP steps read; every wave has then finished the steps
+    // before it, so the stages they read are free, and step j copies K of
+    // tile j + AHEAD and V of tile j + AHEAD - 1 into them.
+    bf16x8 pb[NKB][2];
+    Spec sp;
+    auto fire_all = [&](int kstage, int vstage) {
+      Pend pd;
+      int tv[SPW];
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) tv[j] = trow(sp, j);
+      for (int j = 0; j < SPW; ++j) tv[j] = trow(sp, j);
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          addrs(sp, pd, j, tv[j]);
-          fire(pd, kstage, vstage, j);
-        }
-      };
-      // first tile: QK and softmax only (every kept list has a tile)
-      spec(sp, mring[AHEAD], ering[AHEAD]);
-      if constexpr (BSTEP == 1) wait_first(); else wait_vmcnt<0>();
-      barrier();
-      if constexpr (ACTIVE) {
-        float alpha[QB];
-        float plast;
-        step(F_{}, 0, 0, pb, pb, alpha, plast, sp, AHEAD, AHEAD - 1);
-        if (mring[0] != FULLM) tail_sum(mring[0], plast);
-        rescale(alpha);
-      } else {
-        fire_all(AHEAD, AHEAD - 1);
+      for (int j = 0; j < SPW; ++j) {
+        addrs(sp, pd, j, tv[j]);
+        fire(pd, kstage, vstage, j);
       }
-      shift();
-      int cur = 1, prev = 0;
-      // steady state; the step after the last tile runs the last P.V only
+    };
+    // first tile: QK, then the offset from its row maximum (every kept list
+    // has a tile)
+    spec(sp, mring[AHEAD], ering[AHEAD]);
+    if constexpr (BSTEP == 1) wait_first(); else wait_vmcnt<0>();
+    barrier();
+    if constexpr (ACTIVE) {
+      f32x16 sa[NKB];
+      float ps[4];
+      step(F_{}, F_{}, 0, 0, pb, pb, sa, ps, sp, AHEAD, AHEAD - 1);
+      lrow = raise_offset(sa, pb, true, true);
+      if (mring[0] != FULLM) tail_sum(mring[0], last_p(pb));
+    } else {
+      fire_all(AHEAD, AHEAD - 1);
+    }
+    shift();
+    int cur = 1, prev = 0;
+    // steady state; the step after the last tile runs the last P.V only
 #pragma unroll 1
-      while (true) {
-        const bool have = ering[0];
-        const int fst = cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD;   // K refill
-        const int vfst = fst == 0 ? NSTAGE - 1 : fst - 1;                               // V refill
-        if (have) spec(sp, mring[AHEAD], ering[AHEAD]);
-        // the last P.V reads V of the last tile, copied one step after its K
-        if constexpr (BSTEP == 1) {
-          if (have) wait_first(); else wait_vmcnt<0>();
-          barrier();
-        } else if ((cur & 1) == 0 || !have) {  // every other step, and before the last P.V
-          wait_vmcnt<0>();
-          barrier();
-        }
-        if (!have) {
-          if constexpr (ACTIVE) pv(prev, pb);
-          break;
-        }
-        if constexpr (ACTIVE) {
-          bf16x8 pn[QB][NKB][2];
-          float alpha[QB];
-          float plast;
-          step(T_{}, cur, prev, pb, pn, alpha, plast, sp, fst, vfst);
-          if (mring[0] != FULLM) tail_sum(mring[0], plast);
-          rescale(alpha);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            pb[0][kb][0] = pn[0][kb][0];
-            pb[0][kb][1] = pn[0][kb][1];
-          }
-        } else {
-          fire_all(fst, vfst);
-        }
-        prev = cur;
-        cur = cur + 1 == NSTAGE ? 0 : cur + 1;
-        shift();
+    while (true) {
+      const bool have = ering[0];
+      const int fst = cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD;   // K refill
+      const int vfst = fst == 0 ? NSTAGE - 1 : fst - 1;                               // V refill
+      if (have) spec(sp, mring[AHEAD], ering[AHEAD]);
+      // the last P.V reads V of the last tile, copied one step after its K
+      if constexpr (BSTEP == 1) {
+        if (have) wait_first(); else wait_vmcnt<0>();
+        barrier();
+      } else if ((cur & 1) == 0 || !have) {  // every other step, and before the last P.V
+        wait_vmcnt<0>();
+        barrier();
       }
+      if (!have) {
+        if constexpr (ACTIVE) pv(prev, pb);
+        break;
+      }
+      if constexpr (ACTIVE) {
+        bf16x8 pn[NKB][2];
+        f32x16 sa[NKB];
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        step(T_{}, T_{}, cur, prev, pb, pn, sa, ps, sp, fst, vfst);
+        const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        const bool need = !(psum <= E::kSumLimit);   // NaN or inf included
+        if (__ballot(need) != 0) lrow += raise_offset(sa, pn, need, false);
+        else lrow += psum;
+        if (mring[0] != FULLM) tail_sum(mring[0], last_p(pn));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          pb[kb][0] = pn[kb][0];
+          pb[kb][1] = pn[kb][1];
+        }
+      } else {
+        fire_all(fst, vfst);
+      }
+      prev = cur;
+      cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+      shift();
     }
   };
   if (!wave_active) {
@@ -863,22 +865,19 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q,
   run(T_{});
 
   // ---- normalise and store in raster order
+  const f32x2 hl = halves(lrow);
+  const float inv = 1.f / (hl[0] + hl[1]);
+  if (qrow >= 0) {
+    __bf16* dst = oh + (int64_t)qrow * a.osn + 4 * g;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const f32x2 hl = halves(lrow[qb]);
-    const float inv = 1.f / (hl[0] + hl[1]);
-    if (qrow[qb] >= 0) {
-      __bf16* dst = oh + (int64_t)qrow[qb] * a.osn + 4 * g;
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          u32x2 w;
-          w[0] = E::pack2(oacc[qb][db][4 * r4] * inv, oacc[qb][db][4 * r4 + 1] * inv);
-          w[1] = E::pack2(oacc[qb][db][4 * r4 + 2] * inv, oacc[qb][db][4 * r4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * r4) = w;
-        }
-    }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 w;
+        w[0] = E::pack2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
+        w[1] = E::pack2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * r4) = w;
+      }
   }
 }
 
@@ -905,28 +904,32 @@ int resident_per_xcd(const void* func, int threads, size_t lds) {
   return conc;
 }
 
-template <int D, int NW, int QB, int NSTAGE, int KT, int WPE, bool F16, int BSTEP>
+// LDS bytes of one launch: K and V stages, the slot tables and the
+// kept-block table.
+template <int D, int NSTAGE, int KT>
+size_t attend_lds_bytes(const VsaArgs& a) {
+  return (size_t)2 * NSTAGE * KT * D * 2 + slot_table_bytes(a.gk.V, KT) + (size_t)a.topk * 8;
+}
+
+template <int D, int NW, int NSTAGE, int KT, int WPE, bool F16, int BSTEP>
 hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v, const int32_t* sel, void* o,
                   hipStream_t stream) {
-  // K and V stages, the five slot tables, and the kept list when it fits
-  const size_t lds_base = (size_t)2 * NSTAGE * KT * D * 2 + (size_t)a.gk.V * 20;
-  const bool sel_lds = a.topk <= VSA_ATTEND_SEL_LDS && lds_base + (size_t)a.topk * 8 <= 160 * 1024;
-  const size_t lds = lds_base + (sel_lds ? (size_t)a.topk * 8 : 0);
+  const size_t lds = attend_lds_bytes<D, NSTAGE, KT>(a);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
   if (lds > 65536) {
     static std::atomic<uint64_t> raised{0};
     const hipError_t e = vsa_raise_lds_limit(
-        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16, BSTEP>), raised);
+        reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, NSTAGE, KT, WPE, F16, BSTEP>), raised);
     if (e != hipSuccess) return e;
   }
   VsaArgs b = a;
-  constexpr int RW = NW * 32 * QB;  // query slots per workgroup
+  constexpr int RW = NW * 32;  // query slots per workgroup
   b.tiles = (a.gq.V + RW - 1) / RW;
   const int64_t nunits = (int64_t)a.B * a.Hh * a.nq * b.tiles;
   if (nunits > (int64_t)INT32_MAX / 2 - 64) return hipErrorInvalidValue;
   const int conc = resident_per_xcd(
-      reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16, BSTEP>), NW * 64, lds);
+      reinterpret_cast<const void*>(&vsa_attend_kernel<D, NW, NSTAGE, KT, WPE, F16, BSTEP>), NW * 64, lds);
   if (conc <= 0) return hipErrorInvalidValue;
-  b.sel_lds = sel_lds;
   b.walk_conc = NW == 2 ? conc : 0;   // small-cube kernel: stagger the walks of the resident set
   // Large-cube kernel: when the last round of workgroups on each XCD is at
   // most half full, its units run as half-row workgroups (twice as many,
@@ -935,7 +938,7 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
   const int64_t rem = per_xcd % conc;
   b.split_tail = (NW == 8 && rem > 0 && 2 * rem <= conc) ? (int32_t)rem : 0;
   dim3 grid((unsigned)(8 * (per_xcd + b.split_tail)));
-  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, QB, NSTAGE, KT, WPE, F16, BSTEP>), grid, dim3(NW * 64), lds, stream, b,
+  hipLaunchKernelGGL((vsa_attend_kernel<D, NW, NSTAGE, KT, WPE, F16, BSTEP>), grid, dim3(NW * 64), lds, stream, b,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o);
   return hipGetLastError();
 }
@@ -943,21 +946,23 @@ hipError_t launch(const VsaArgs& a, const void* q, const void* k, const void* v,
 }  // namespace
 
 // Tilings, all on the pipelined step: cubes of up to 64 tokens use 2-wave
-// workgroups (64 query rows) with 32-key tiles in rings of two (32 KB of LDS
-// for D = 128, so four workgroups share a CU) and a barrier per tile; larger
-// cubes use 8-wave workgroups (256 query rows) with 64-key tiles, for
-// D = 128 in rings of four with one barrier per two tiles (128 KB; 1-2%
-// faster than rings of two with a barrier per tile), for D = 64 in rings of
-// three with a barrier per tile.
+// workgroups (64 query rows) with 32-key tiles in rings of two (32 KB of
+// K/V stages for D = 128, so four workgroups share a CU) and a barrier per
+// tile; larger cubes use 8-wave workgroups (256 query rows) with 64-key
+// tiles, for D = 128 in rings of four with one barrier per two tiles
+// (128 KB), or in rings of two with a barrier per tile when the slot and
+// kept-block tables leave no room for four; for D = 64 in rings of three
+// with a barrier per tile.
 template <bool F16>
 static hipError_t dispatch(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                            const int32_t* sel, void* o, hipStream_t stream) {
   if (a.D == 128) {
-    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 1, 2, 32, 2, F16, 1>(a, q, k, v, sel, o, stream);
-    return launch<128, 8, 1, 4, 64, 2, F16, 2>(a, q, k, v, sel, o, stream);
+    if (variant == VSA_ATTEND_ROWS64) return launch<128, 2, 2, 32, 2, F16, 1>(a, q, k, v, sel, o, stream);
+    if (attend_lds_bytes<128, 4, 64>(a) <= 160 * 1024) return launch<128, 8, 4, 64, 2, F16, 2>(a, q, k, v, sel, o, stream);
+    return launch<128, 8, 2, 64, 2, F16, 1>(a, q, k, v, sel, o, stream);
   }
-  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 1, 2, 32, 2, F16, 1>(a, q, k, v, sel, o, stream);
-  return launch<64, 8, 1, 3, 64, 2, F16, 1>(a, q, k, v, sel, o, stream);
+  if (variant == VSA_ATTEND_ROWS64) return launch<64, 2, 2, 32, 2, F16, 1>(a, q, k, v, sel, o, stream);
+  return launch<64, 8, 3, 64, 2, F16, 1>(a, q, k, v, sel, o, stream);
 }
 
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,

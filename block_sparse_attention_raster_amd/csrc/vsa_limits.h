@@ -9,7 +9,6 @@
 #define VSA_SELECT_MAX_ROWS 16        /* query blocks per score/top-k group    */
 #define VSA_SELECT_SCORE_LDS 65536    /* bytes of LDS for one group's scores   */
 #define VSA_SELECT_MFMA_MAX_BLOCKS 2048 /* cubes scored on the matrix cores    */
-#define VSA_ATTEND_SEL_LDS 4096       /* kept lists up to this long sit in LDS */
 
 enum {
   VSA_ATTEND_ROWS64 = 1,   /* 64 query rows per workgroup (cubes <= 64 tokens) */
