@@ -1,15 +1,24 @@
-"""Benchmark: one step = one whole attention call (vsa_select + vsa_attend over
-every (batch, head)) of the block-sparse path on synthetic inputs resident in
-HBM. Prints one JSON line.
+"""Benchmark: one step = one whole attention call (pool, score + top-k, and
+block-sparse attention over every (batch, head): vsa_select + vsa_attend,
+with vsa_select issued as its two halves vsa_pool and vsa_score_topk so that
+an event can sit between them) on synthetic inputs resident in HBM. Prints
+one JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload wan] [--dtype bf16]
 
 Throughput is selected-block TFLOP/s: 4 * head_dim * sum over query tokens of
 the number of key tokens in their kept blocks (QK^T and PV; the selection of
-the GPU's own run), divided by the measured time. The roofline object is for
-the attention kernel (the dominant one), timed with HIP events on the stream
-it runs on. The cpu_baseline object times the CPU oracle (float64,
-dense-masked) on a bounded sample of the same workload and scales it to the
+the GPU's own run), divided by the measured time. ``value`` and
+``ms_per_step`` are the wall clock of the timed steps run back to back; HIP
+events on the stream the kernels run on split every step into pool, score +
+top-k and attention (median and mean over the steps). A second pass runs the
+same steps with the L2 and the MALL flushed before each (a 1 GiB buffer
+written outside the timed region), as between the layers of a real model.
+The roofline object is for the attention kernel (the dominant one). The
+other workloads of the suite (wan_sweep at top-k 16, 32 and 120, long720p,
+prefix) are timed in the same run and reported under ``suite``. The
+cpu_baseline object times the CPU oracle (float64, dense-masked) on a
+sample of whole (batch, head) pairs, one per host core, and scales it to the
 whole call.
 """
 from __future__ import annotations
@@ -18,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -33,6 +43,7 @@ PEAK_MFMA_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": 2500.0}   # fp16 dense peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend.json")
 ATTEND_SOURCES = ["attend.hip", "vsa_device.h", "vsa_limits.h"]
+SUITE = (("wan_sweep", 16), ("wan_sweep", 32), ("wan_sweep", 120), ("long720p", None), ("prefix", None))
 
 
 def attend_source_hash() -> str:
@@ -52,11 +63,26 @@ def attend_source_hash() -> str:
 
 
 def selected_flops(pl, sel_np: np.ndarray) -> float:
-    """4 * D * sum_i n_i * (P + sum_{j in S_i} m_j) over every (b, h)."""
-    counts = pl.valid_counts()
-    m = counts[pl.num_prefix_blocks:]
+    """4 * D * sum_i n_i * (P + sum_{j in S_i} m_j) over every (b, h): n_i
+    the valid tokens of query block i (q's grid), m_j those of key cube j
+    (the key grid), P the prefix tokens every block keeps."""
+    nq = pl.valid_counts("q")
+    m = pl.valid_counts("k")[pl.num_prefix_blocks_k:]
     kept = pl.prefix_len + m[sel_np].sum(axis=-1)           # [B, Hh, nq]
-    return float(4.0 * pl.head_dim * np.sum(kept * counts[None, None, :]))
+    return float(4.0 * pl.head_dim * np.sum(kept * nq[None, None, :]))
+
+
+def pool_bytes(pl) -> float:
+    """Algorithmic bytes of the pooling kernel: q and k read once (2-byte
+    elements), the float32 means written."""
+    BH = pl.batch * pl.heads
+    return float(BH * pl.head_dim * (2 * (pl.seq_len + pl.seq_len_k) + 4 * (pl.num_q_blocks + pl.num_blocks)))
+
+
+def select_bytes(pl) -> float:
+    """Algorithmic bytes of score + top-k: the means read, sel written."""
+    BH = pl.batch * pl.heads
+    return float(BH * (4 * pl.head_dim * (pl.num_q_blocks + pl.num_blocks) + 4 * pl.num_q_blocks * pl.topk))
 
 
 def traffic_for(workload: str):
@@ -72,61 +98,127 @@ def traffic_for(workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, bits, sel_np, flops_total, budget_s: float = 12.0, dtype: str = "bf16"):
-    """Time the CPU oracle (float64, dense-masked) on whole (batch, head)
-    pairs: pool + score + top-k of the head and attention of all its query
-    blocks, head after head until about ``budget_s`` seconds have been spent
-    (at least one head; for very large heads, a prefix of its query blocks).
-    The per-head time is scaled to the whole call."""
-    from oracle import vsa_oracle as O
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _blas() -> str:
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
     except Exception:  # pragma: no cover - informational only
-        threads = len(os.sched_getaffinity(0))
-    g = O.geometry(w.latent, w.cube, w.prefix_len)
-    q_b, k_b, v_b = bits
+        return "unknown"
+
+
+def cpu_baseline(w, bits, flops_total, dtype: str = "bf16", cores: int = None):
+    """Time the CPU oracle (float64, dense-masked; pool, score, top-k, then
+    attention of every query block) on whole (batch, head) pairs, one per
+    worker process with one BLAS thread each, as many pairs as cores (at
+    most all of them), and scale the wall time to the whole call."""
+    from oracle import parallel as OP
+    cores = cores or OP.host_cores()
     BH = w.batch * w.heads
-    spent, heads_done, partial = 0.0, 0, None
-    for bh in range(BH):
-        b, h = divmod(bh, w.heads)
-        t0 = time.perf_counter()
-        qf, kf, vf = (O.decode(x[b, h], dtype) for x in (q_b, k_b, v_b))
-        s = O.block_scores(O.pool(qf, g), O.pool(kf, g, video_only=True), w.head_dim)
-        sel0 = O.select_topk(s, w.topk)
-        t_sel = time.perf_counter() - t0
-        t_att, nblk = 0.0, 0
-        for i in range(g.num_q_blocks):
-            t1 = time.perf_counter()
-            O.attend_dense_masked(qf, kf, vf, sel0, g, query_blocks=[i])
-            t_att += time.perf_counter() - t1
-            nblk += 1
-            if heads_done == 0 and t_sel + t_att > budget_s:
-                break
-        if nblk < g.num_q_blocks:      # one head is more than the budget
-            partial = (t_sel, t_att, nblk)
-            break
-        spent += t_sel + t_att
-        heads_done += 1
-        if spent > budget_s:
-            break
-    if partial is not None:
-        t_sel, t_att, nblk = partial
-        per_head = t_sel + t_att / nblk * g.num_q_blocks
-        sample = (f"(batch 0, head 0) of {BH}: float64 pool+score+top-k of the head ({t_sel:.2f} s) and "
-                  f"dense-masked attention of {nblk} of {g.num_q_blocks} query blocks ({t_att:.2f} s)")
-    else:
-        per_head = spent / heads_done
-        sample = (f"{heads_done} of {BH} (batch, head) pairs in full: float64 pool+score+top-k and "
-                  f"dense-masked attention of all {g.num_q_blocks} query blocks ({spent:.2f} s)")
-    est_s = BH * per_head
+    n = min(BH, cores)
+    pairs = [divmod(i, w.heads) for i in range(n)]
+    jobs = OP.head_jobs(bits, pairs, dtype=dtype, latent=w.latent, cube=w.cube, prefix_len=w.prefix_len,
+                        topk=w.topk)
+    t0 = time.perf_counter()
+    res = OP.map_jobs(OP.time_head, jobs, workers=n)
+    wall = time.perf_counter() - t0
+    rounds = -(-BH // n)                     # the whole call in rounds of n pairs
+    est_s = wall * rounds
+    sel_s = float(np.mean([r["select_s"] for r in res]))
     return {
         "value": flops_total / est_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(n),
         "kind": "oracle",
         "ms_per_call_est": est_s * 1e3,
-        "sample": sample + ", scaled to the whole call",
+        "select_ms_per_head": sel_s * 1e3,
+        "cpu_model": _cpu_model(),
+        "blas": _blas(),
+        "peak_rss_mib_per_worker": max(r["peak_rss_mib"] for r in res),
+        "host_cores": int(cores),
+        "sample": (f"{n} of {BH} (batch, head) pairs in parallel, one process and one BLAS thread each: "
+                   f"float64 pool+score+top-k and dense-masked attention of all query blocks "
+                   f"({wall:.2f} s wall), scaled by {rounds} rounds to the whole call"),
+    }
+
+
+class Run:
+    """One workload on the GPU: inputs, plan, buffers and an event-timed
+    step issued as vsa_pool, vsa_score_topk, vsa_attend."""
+
+    def __init__(self, w, topk, dtype, dev, bits=None):
+        import torch
+        import block_sparse_attention_raster_amd as vsa
+        from block_sparse_attention_raster_amd import synthetic
+        self.vsa, self.torch, self.w, self.topk, self.dtype = vsa, torch, w, topk, dtype
+        self.bits = synthetic.make_inputs(w, dtype=dtype) if bits is None else bits
+        self.q, self.k, self.v = (synthetic.bits_to_torch(x, dev, dtype) for x in self.bits)
+        self.pl = vsa.plan_for(self.q, w.latent, w.cube, topk, w.prefix_len)
+        self.ws = torch.empty(self.pl.workspace_bytes, dtype=torch.uint8, device=dev)
+        self.sel = torch.empty((self.pl.batch, self.pl.heads, self.pl.num_q_blocks, topk), dtype=torch.int32,
+                               device=dev)
+        self.out = torch.empty_like(self.q)
+
+    def step(self, ev=None):
+        vsa, pl = self.vsa, self.pl
+        if ev is not None:
+            ev[0].record()
+        vsa.pool(pl, self.q, self.k, self.ws)
+        if ev is not None:
+            ev[1].record()
+        vsa.score_topk(pl, self.ws, self.sel)
+        if ev is not None:
+            ev[2].record()
+        vsa.attend(pl, self.q, self.k, self.v, self.sel, self.out)
+        if ev is not None:
+            ev[3].record()
+
+    def timed(self, steps, flush=None):
+        """Events of `steps` steps; with `flush`, a buffer write before each
+        step, outside its events. Returns (per-step ms [steps, 4 phases:
+        pool, score, attend, call], wall ms of the loop)."""
+        torch = self.torch
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush is not None:
+                flush.zero_()
+            self.step(events[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]),
+                        e[0].elapsed_time(e[3])] for e in events])
+        return ms, wall
+
+    def flops(self):
+        return selected_flops(self.pl, self.sel.cpu().numpy().astype(np.int64))
+
+    def free(self):
+        del self.q, self.k, self.v, self.ws, self.sel, self.out
+        self.torch.cuda.empty_cache()
+
+
+def _phase_stats(ms, flops, pl, peak):
+    med = np.median(ms, axis=0)
+    return {
+        "ms_per_call_median": float(med[3]), "pool_ms": float(med[0]), "select_ms": float(med[1]),
+        "attend_ms": float(med[2]),
+        "attend_tflops": flops / (med[2] * 1e-3) / 1e12,
+        "attend_pct_bf16_peak": 100.0 * flops / (med[2] * 1e-3) / 1e12 / peak,
+        "pool_gbs": pool_bytes(pl) / (med[0] * 1e-3) / 1e9,
+        "select_gbs": select_bytes(pl) / (med[1] * 1e-3) / 1e9,
     }
 
 
@@ -140,6 +232,9 @@ def main(argv=None):
     ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
                     help="element type of q, k, v and the output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-suite", action="store_true", help="time the headline workload only")
+    ap.add_argument("--suite-steps", type=int, default=10)
+    ap.add_argument("--flush-mib", type=int, default=1024, help="buffer written before each flushed step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters)")
@@ -152,7 +247,6 @@ def main(argv=None):
         return 2
 
     import torch
-    import block_sparse_attention_raster_amd as vsa
     from block_sparse_attention_raster_amd import synthetic
 
     if args.calibrate_copy:
@@ -164,50 +258,32 @@ def main(argv=None):
         print(json.dumps({"copy_bytes": src.numel(), "repeats": 3}), flush=True)
         return 0
 
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    peak = PEAK_MFMA_TFLOPS[args.dtype]
     w = synthetic.WORKLOADS[args.workload]
     topk = args.topk if args.topk is not None else w.topk
     if topk != w.topk:
         w = synthetic.Workload(w.name, w.seed, w.batch, w.heads, w.head_dim, w.latent, w.cube,
                                (topk,), w.prefix_len, w.modification)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    bits = synthetic.make_inputs(w, dtype=args.dtype)
-    q, k, v = (synthetic.bits_to_torch(x, dev, args.dtype) for x in bits)
-    pl = vsa.plan_for(q, w.latent, w.cube, topk, w.prefix_len)
-    ws = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
-    sel = torch.empty((pl.batch, pl.heads, pl.num_q_blocks, topk), dtype=torch.int32, device=dev)
-    out = torch.empty_like(q)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        vsa.select(pl, q, k, ws, sel)
-        if ev is not None:
-            ev[1].record()
-        vsa.attend(pl, q, k, v, sel, out)
-        if ev is not None:
-            ev[2].record()
-
+    run = Run(w, topk, args.dtype, dev)
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-
-    sel_np = sel.cpu().numpy().astype(np.int64)
-    flops = selected_flops(pl, sel_np)
+        run.step()
+    # the timed steps, back to back (the metric's wall clock), then the
+    # same steps with the caches flushed before each
+    ms, wall = run.timed(args.steps)
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+    ms_flushed, _ = run.timed(args.steps, flush=flush)
+    del flush
+    torch.cuda.empty_cache()
+    ms_per_step = wall / args.steps
+    flops = run.flops()
+    pl = run.pl
     value = flops / (ms_per_step * 1e-3) / 1e12
-    att_tflops = flops / (att_ms * 1e-3) / 1e12
+    warm = _phase_stats(ms, flops, pl, peak)
+    cold = _phase_stats(ms_flushed, flops, pl, peak)
+    att_tflops = warm["attend_tflops"]
     traffic = traffic_for(w.name if args.dtype == "bf16" else f"{w.name}_{args.dtype}")
-    peak = PEAK_MFMA_TFLOPS[args.dtype]
     line = {
         "metric": METRIC,
         "value": value,
@@ -228,11 +304,20 @@ def main(argv=None):
             "parallelism": "single GPU",
         },
         "ms_per_call": ms_per_step,
-        "select_ms": sel_ms,
-        "attend_ms": att_ms,
+        "ms_per_call_median": warm["ms_per_call_median"],
+        "ms_per_call_mean": float(np.mean(ms[:, 3])),
+        "pool_ms": warm["pool_ms"],
+        "select_ms": warm["select_ms"],
+        "attend_ms": warm["attend_ms"],
+        "attend_ms_mean": float(np.mean(ms[:, 2])),
+        "pool_gbs": warm["pool_gbs"],
+        "select_gbs": warm["select_gbs"],
         "selected_flop": flops,
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "attend_pct_bf16_peak": 100.0 * att_tflops / PEAK_BF16_TFLOPS,
+        "attend_pct_bf16_peak": warm["attend_pct_bf16_peak"],
+        "flushed": {k: cold[k] for k in ("ms_per_call_median", "pool_ms", "select_ms", "attend_ms",
+                                         "attend_pct_bf16_peak", "pool_gbs", "select_gbs")},
+        "flush_bytes": args.flush_mib << 20,
         "roofline": {
             "bound": "mfma", "achieved": att_tflops, "peak": peak, "unit": "TFLOP/s",
             "frac": att_tflops / peak,
@@ -240,8 +325,33 @@ def main(argv=None):
             "kernel": "vsa_attend_kernel",
         },
     }
+    bits, wl = run.bits, run.w
+    run.free()
+    del run
+    if not args.no_suite:
+        suite = {}
+        cache = {}
+        for name, tk in SUITE:
+            ws = synthetic.WORKLOADS[name]
+            tk = tk or ws.topk
+            key = f"{name}_{tk}" if name == "wan_sweep" else name
+            if name not in cache:
+                cache.clear()
+                cache[name] = synthetic.make_inputs(ws, dtype=args.dtype)
+            r = Run(ws, tk, args.dtype, dev, bits=cache[name])
+            for _ in range(2):
+                r.step()
+            sms, swall = r.timed(args.suite_steps)
+            sf = r.flops()
+            st = _phase_stats(sms, sf, r.pl, peak)
+            st.update({"ms_per_call": swall / args.suite_steps, "steps": args.suite_steps, "selected_flop": sf,
+                       "topk": tk, "num_blocks": r.pl.num_blocks,
+                       "pct_bf16_peak": 100.0 * sf / (swall / args.suite_steps * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+            suite[key] = st
+            r.free()
+        line["suite"] = suite
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, bits, sel_np, flops, dtype=args.dtype)
+        line["cpu_baseline"] = cpu_baseline(wl, bits, flops, dtype=args.dtype)
     print(json.dumps(line), flush=True)
     return 0
 

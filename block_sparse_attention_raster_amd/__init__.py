@@ -23,7 +23,7 @@ from typing import Optional, Sequence, Tuple
 from . import _lib
 from ._lib import VsaError
 
-__all__ = ["Plan", "Route", "VsaError", "plan", "plan_for", "select", "attend", "forward",
+__all__ = ["Plan", "Route", "VsaError", "plan", "plan_for", "select", "pool", "score_topk", "attend", "forward",
            "flash_attn_bsa_3d", "topk_for_sparsity", "route", "describe"]
 
 
@@ -49,21 +49,20 @@ class Plan:
 
     def valid_counts(self, side: str = "q"):
         """Valid token count of every block (prefix blocks, then cubes) of
-        q's grid (``side="q"``) or of k's (``"k"``). Host-side, numpy."""
+        q's grid (``side="q"``) or of k's (``"k"``), from vsa_block_counts;
+        an int64 numpy array."""
         import numpy as np
-        if side == "q":
-            (T, H, W), (ct, ch, cw), nblk = self.latent, self.cube, self.nblk
-            V, Pb = self.cube_volume, self.num_prefix_blocks
-        elif side == "k":
-            (T, H, W), (ct, ch, cw), nblk = self.latent_k, self.cube_k, self.nblk_k
-            V, Pb = self.cube_volume_k, self.num_prefix_blocks_k
-        else:
+        sides = {"q": _lib.VSA_SIDE_Q, "k": _lib.VSA_SIDE_K}
+        if side not in sides:
             raise ValueError("side must be 'q' or 'k'")
-        P = self.prefix_len
-        pre = [min(V, P - i * V) for i in range(Pb)]
-        ax = [np.minimum(c, L - np.arange(n) * c) for L, c, n in zip((T, H, W), (ct, ch, cw), nblk)]
-        vid = (ax[0][:, None, None] * ax[1][None, :, None] * ax[2][None, None, :]).reshape(-1)
-        return np.concatenate([np.array(pre, dtype=np.int64), vid.astype(np.int64)])
+        L = _lib.lib()
+        n = L.vsa_block_counts(ctypes.byref(self.raw), sides[side], None, 0)
+        if n < 0:
+            raise VsaError(n, "vsa_block_counts")
+        buf = (ctypes.c_int32 * n)()
+        _lib.check(0 if L.vsa_block_counts(ctypes.byref(self.raw), sides[side], buf, n) == n else -1,
+                   "vsa_block_counts")
+        return np.frombuffer(buf, dtype=np.int32).astype(np.int64)
 
     def __repr__(self):
         return f"Plan({describe(self)})"
@@ -95,19 +94,13 @@ def _problem(batch, heads, head_dim, latent, cube, topk, prefix_len=0, strides=N
              dtype="bf16", latent_k=None, cube_k=None, kv_strides=None) -> _lib.VsaProblem:
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be one of {sorted(_DTYPES)}, got {dtype!r}")
-    N = int(prefix_len) + int(latent[0]) * int(latent[1]) * int(latent[2])
-    if strides is None:
-        strides = (heads * N * head_dim, N * head_dim, head_dim)
-    if o_strides is None:
-        o_strides = strides
-    latent_k = tuple(latent) if latent_k is None else tuple(latent_k)
-    cube_k = tuple(cube) if cube_k is None else tuple(cube_k)
-    if kv_strides is None:
-        if latent_k == tuple(latent):
-            kv_strides = strides
-        else:
-            Nk = int(prefix_len) + int(latent_k[0]) * int(latent_k[1]) * int(latent_k[2])
-            kv_strides = (heads * Nk * head_dim, Nk * head_dim, head_dim)
+    # zeros ask vsa_plan for its default layout (contiguous; o like q; k and
+    # v like q on q's grid, else contiguous on their own grid)
+    strides = (0, 0, 0) if strides is None else strides
+    o_strides = (0, 0, 0) if o_strides is None else o_strides
+    kv_strides = (0, 0, 0) if kv_strides is None else kv_strides
+    latent_k = (0, 0, 0) if latent_k is None else tuple(latent_k)
+    cube_k = (0, 0, 0) if cube_k is None else tuple(cube_k)
     pr = _lib.VsaProblem()
     pr.batch, pr.heads, pr.head_dim = int(batch), int(heads), int(head_dim)
     pr.latent[:] = [int(x) for x in latent]
@@ -126,14 +119,20 @@ def _torch_dtype(pl: Plan):
     return torch.float16 if pl.dtype == _lib.VSA_DTYPE_F16 else torch.bfloat16
 
 
-def _check_qkv(t, name, shape, strides, dtype):
+def _check_device(t, name, device):
+    """Every buffer the kernels touch must live on q's GPU: a host pointer
+    or another device's memory would reach the kernels unchecked."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the GPU device of q ({device}), got {t.device}")
+
+
+def _check_qkv(t, name, shape, strides, dtype, device=None):
+    _check_device(t, name, device)
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (the plan's dtype), got {t.dtype}")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.stride(3) != 1 or tuple(t.stride()[:3]) != tuple(strides):
@@ -162,31 +161,76 @@ def _stream_ptr(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _qk_checked(pl: Plan, q, k):
+    shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
+    kshape = (pl.batch, pl.heads, pl.seq_len_k, pl.head_dim)
+    dt = _torch_dtype(pl)
+    _check_qkv(q, "q", shape, (pl.stride_b, pl.stride_h, pl.stride_n), dt)
+    _check_qkv(k, "k", kshape, pl.kv_strides, dt, q.device)
+    return q.device
+
+
+def _workspace_checked(pl: Plan, workspace, dev):
+    import torch
+    if workspace is None:
+        return torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
+    _check_device(workspace, "workspace", dev)
+    if workspace.numel() * workspace.element_size() < pl.workspace_bytes or not workspace.is_contiguous():
+        raise ValueError("workspace too small or not contiguous")
+    return workspace
+
+
+def _sel_checked(pl: Plan, sel, dev):
+    import torch
+    if sel is None:
+        return torch.empty((pl.batch, pl.heads, pl.num_q_blocks, pl.topk), dtype=torch.int32, device=dev)
+    _check_device(sel, "sel", dev)
+    if sel.dtype != torch.int32 or sel.numel() != pl.sel_elems or not sel.is_contiguous():
+        raise ValueError("sel must be a contiguous int32 tensor of plan.sel_elems elements")
+    return sel
+
+
 def select(pl: Plan, q, k, workspace=None, sel=None):
     """Pool, score and select (vsa_select). Returns (sel, workspace):
     sel int32 [B, heads, num_q_blocks, topk] ascending cube ids; workspace
     holds float32 qbar then kbar (see include/vsa.h)."""
     import torch
-    shape = (pl.batch, pl.heads, pl.seq_len, pl.head_dim)
-    strides = (pl.stride_b, pl.stride_h, pl.stride_n)
-    kshape = (pl.batch, pl.heads, pl.seq_len_k, pl.head_dim)
-    dt = _torch_dtype(pl)
-    _check_qkv(q, "q", shape, strides, dt)
-    _check_qkv(k, "k", kshape, pl.kv_strides, dt)
-    dev = q.device
-    if workspace is None:
-        workspace = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
-    elif workspace.numel() * workspace.element_size() < pl.workspace_bytes or not workspace.is_contiguous():
-        raise ValueError("workspace too small or not contiguous")
-    if sel is None:
-        sel = torch.empty((pl.batch, pl.heads, pl.num_q_blocks, pl.topk), dtype=torch.int32, device=dev)
-    elif sel.dtype != torch.int32 or sel.numel() != pl.sel_elems or not sel.is_contiguous():
-        raise ValueError("sel must be a contiguous int32 tensor of plan.sel_elems elements")
+    dev = _qk_checked(pl, q, k)
+    workspace = _workspace_checked(pl, workspace, dev)
+    sel = _sel_checked(pl, sel, dev)
     with torch.cuda.device(dev):
         st = _lib.lib().vsa_select(ctypes.byref(pl.raw), q.data_ptr(), k.data_ptr(), workspace.data_ptr(),
                                    sel.data_ptr(), _stream_ptr(dev))
     _lib.check(st, "vsa_select")
     return sel, workspace
+
+
+def pool(pl: Plan, q, k, workspace=None):
+    """The pooling half of select (vsa_pool): qbar and kbar into the
+    workspace, which is returned."""
+    import torch
+    dev = _qk_checked(pl, q, k)
+    workspace = _workspace_checked(pl, workspace, dev)
+    with torch.cuda.device(dev):
+        st = _lib.lib().vsa_pool(ctypes.byref(pl.raw), q.data_ptr(), k.data_ptr(), workspace.data_ptr(),
+                                 _stream_ptr(dev))
+    _lib.check(st, "vsa_pool")
+    return workspace
+
+
+def score_topk(pl: Plan, workspace, sel=None):
+    """The selection half of select (vsa_score_topk): scores the pooled
+    means the workspace holds and writes the kept cube ids; returns sel."""
+    import torch
+    _check_device(workspace, "workspace", None)
+    dev = workspace.device
+    workspace = _workspace_checked(pl, workspace, dev)
+    sel = _sel_checked(pl, sel, dev)
+    with torch.cuda.device(dev):
+        st = _lib.lib().vsa_score_topk(ctypes.byref(pl.raw), workspace.data_ptr(), sel.data_ptr(),
+                                       _stream_ptr(dev))
+    _lib.check(st, "vsa_score_topk")
+    return sel
 
 
 def attend(pl: Plan, q, k, v, sel, out=None):
@@ -197,14 +241,15 @@ def attend(pl: Plan, q, k, v, sel, out=None):
     kshape = (pl.batch, pl.heads, pl.seq_len_k, pl.head_dim)
     dt = _torch_dtype(pl)
     _check_qkv(q, "q", shape, strides, dt)
-    for t, n in ((k, "k"), (v, "v")):
-        _check_qkv(t, n, kshape, pl.kv_strides, dt)
     dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _check_qkv(t, n, kshape, pl.kv_strides, dt, dev)
     if out is None:
         out = torch.empty_strided(shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n, 1),
                                   dtype=dt, device=dev)
     else:
-        _check_qkv(out, "out", shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n), dt)
+        _check_qkv(out, "out", shape, (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n), dt, dev)
+    _check_device(sel, "sel", dev)
     if sel.dtype != torch.int32 or sel.numel() != pl.sel_elems or not sel.is_contiguous():
         raise ValueError("sel must be a contiguous int32 tensor of plan.sel_elems elements")
     with torch.cuda.device(dev):
@@ -226,8 +271,8 @@ def forward(q, k, v, latent_shape: Sequence[int], cube_shape: Sequence[int], top
 
 
 def topk_for_sparsity(num_blocks: int, sparsity: float) -> int:
-    """Key cubes kept for a sparsity in [0, 1) (vsa_topk_for_sparsity): the
-    nearest integer to num_blocks * (1 - sparsity), halves up, at least 1."""
+    """Key cubes kept for a sparsity in [0, 1) (vsa_topk_for_sparsity):
+    floor(num_blocks * (1 - sparsity)), at least 1."""
     r = _lib.lib().vsa_topk_for_sparsity(int(num_blocks), float(sparsity))
     if r < 0:
         raise VsaError(r, "vsa_topk_for_sparsity")
@@ -246,10 +291,11 @@ def flash_attn_bsa_3d(q, k, v, latent_shape_q: Sequence[int], latent_shape_k: Se
     if (sparsity is None) == (topk is None):
         raise ValueError("give exactly one of sparsity and topk")
     if topk is None:
-        nb_k = 1
-        for L, c in zip(latent_shape_k, chunk_3d_shape_k):
-            nb_k *= -(-int(L) // int(c))
-        topk = topk_for_sparsity(nb_k, sparsity)
+        # the key-chunk count from a plan of the problem (top-k 1 is always
+        # valid); the sparsity then fixes top-k
+        probe = plan_for(q, latent_shape_q, chunk_3d_shape_q, 1, prefix_len, out, k, latent_shape_k,
+                         chunk_3d_shape_k)
+        topk = topk_for_sparsity(probe.num_blocks, sparsity)
     return forward(q, k, v, latent_shape_q, chunk_3d_shape_q, topk, prefix_len, out,
                    latent_shape_k=latent_shape_k, cube_shape_k=chunk_3d_shape_k)
 

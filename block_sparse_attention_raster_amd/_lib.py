@@ -17,9 +17,12 @@ VSA_ERR_DEVICE = -6
 VSA_ERR_LAUNCH = -7
 VSA_DTYPE_BF16 = 0
 VSA_DTYPE_F16 = 1
+VSA_SIDE_Q = 0
+VSA_SIDE_K = 1
 
 EXPORTED = ("vsa_plan", "vsa_topk_for_sparsity", "vsa_select", "vsa_attend", "vsa_forward",
-            "vsa_describe", "vsa_status_str", "vsa_route", "vsa_describe_route")
+            "vsa_describe", "vsa_status_str", "vsa_route", "vsa_describe_route", "vsa_block_counts",
+            "vsa_pool", "vsa_score_topk")
 
 VSA_ROUTE_VSA = 0
 VSA_ROUTE_VSA_ALL_BLOCKS = 1
@@ -94,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.vsa_topk_for_sparsity.restype = ctypes.c_int
         L.vsa_select.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp]
         L.vsa_select.restype = ctypes.c_int
+        L.vsa_pool.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp]
+        L.vsa_pool.restype = ctypes.c_int
+        L.vsa_score_topk.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp]
+        L.vsa_score_topk.restype = ctypes.c_int
         L.vsa_attend.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp, vp]
         L.vsa_attend.restype = ctypes.c_int
         L.vsa_forward.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp, vp, vp]
@@ -104,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.vsa_route.restype = ctypes.c_int
         L.vsa_describe_route.argtypes = [ctypes.POINTER(VsaRoute), ctypes.c_char_p, ctypes.c_size_t]
         L.vsa_describe_route.restype = ctypes.c_int
+        L.vsa_block_counts.argtypes = [ctypes.POINTER(VsaPlan), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.c_int64]
+        L.vsa_block_counts.restype = ctypes.c_int
         L.vsa_status_str.argtypes = [ctypes.c_int]
         L.vsa_status_str.restype = ctypes.c_char_p
         _lib = L

@@ -118,22 +118,42 @@ VsaArgs make_args(const vsa_plan_t& pl) {
 
 }  // namespace
 
-extern "C" int vsa_select(const vsa_plan_t* plan, const void* q, const void* k, void* workspace,
-                          int32_t* sel, void* stream) {
+extern "C" int vsa_pool(const vsa_plan_t* plan, const void* q, const void* k, void* workspace, void* stream) {
   int st = check_plan(plan);
   if (st != VSA_OK) return st;
-  if (q == nullptr || k == nullptr || workspace == nullptr || sel == nullptr) return VSA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      (reinterpret_cast<uintptr_t>(sel) & 3u) != 0)
+  if (q == nullptr || k == nullptr || workspace == nullptr) return VSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return VSA_ERR_ALIGN;
   if ((st = check_device()) != VSA_OK) return st;
   const VsaArgs a = make_args(*plan);
   float* qbar = static_cast<float*>(workspace);
   float* kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->kbar_offset);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (vsa_launch_pool(a, q, k, qbar, kbar, s) != hipSuccess) return VSA_ERR_LAUNCH;
-  if (vsa_launch_score_topk(a, qbar, kbar, sel, s) != hipSuccess) return VSA_ERR_LAUNCH;
+  if (vsa_launch_pool(a, q, k, qbar, kbar, static_cast<hipStream_t>(stream)) != hipSuccess) return VSA_ERR_LAUNCH;
   return VSA_OK;
+}
+
+extern "C" int vsa_score_topk(const vsa_plan_t* plan, const void* workspace, int32_t* sel, void* stream) {
+  int st = check_plan(plan);
+  if (st != VSA_OK) return st;
+  if (workspace == nullptr || sel == nullptr) return VSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(sel) & 3u) != 0)
+    return VSA_ERR_ALIGN;
+  if ((st = check_device()) != VSA_OK) return st;
+  const VsaArgs a = make_args(*plan);
+  const float* qbar = static_cast<const float*>(workspace);
+  const float* kbar = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + plan->kbar_offset);
+  if (vsa_launch_score_topk(a, qbar, kbar, sel, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return VSA_ERR_LAUNCH;
+  return VSA_OK;
+}
+
+extern "C" int vsa_select(const vsa_plan_t* plan, const void* q, const void* k, void* workspace,
+                          int32_t* sel, void* stream) {
+  if (q == nullptr || k == nullptr || workspace == nullptr || sel == nullptr) return VSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(sel) & 3u) != 0) return VSA_ERR_ALIGN;
+  const int st = vsa_pool(plan, q, k, workspace, stream);
+  if (st != VSA_OK) return st;
+  return vsa_score_topk(plan, workspace, sel, stream);
 }
 
 extern "C" int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k, const void* v,

@@ -12,6 +12,7 @@
 // lie on different grids with different cube shapes, and a sparsity maps to
 // a top-k (the "fastbsa" package page, section "Use").
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cmath>
@@ -95,19 +96,34 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   if (p.batch < 1 || p.heads < 1 || p.head_dim < 1 || p.prefix_len < 0) return VSA_ERR_INVALID_ARG;
   for (int a = 0; a < 3; ++a)
     if (p.latent[a] < 1 || p.cube[a] < 1) return VSA_ERR_INVALID_ARG;
-  if (p.stride_b < 1 || p.stride_h < 1 || p.stride_n < 1 || p.o_stride_b < 1 ||
-      p.o_stride_h < 1 || p.o_stride_n < 1)
-    return VSA_ERR_INVALID_ARG;
-  // key side: unset groups take q's values
+  // Stride groups are all zero (a default) or all >= 1. Defaults: q
+  // contiguous [B][Hh][N][D]; o as q; k and v as q on q's grid, else
+  // contiguous on their own grid.
+  const int64_t qs[3] = {p.stride_b, p.stride_h, p.stride_n};
+  const int64_t os[3] = {p.o_stride_b, p.o_stride_h, p.o_stride_n};
   const int64_t kvs[3] = {p.kv_stride_b, p.kv_stride_h, p.kv_stride_n};
+  const int gq = group_state(qs, 3), go = group_state(os, 3);
   const int gl = group_state(p.latent_k, 3), gc = group_state(p.cube_k, 3), gs = group_state(kvs, 3);
-  if (gl < 0 || gc < 0 || gs < 0) return VSA_ERR_INVALID_ARG;
+  if (gq < 0 || go < 0 || gl < 0 || gc < 0 || gs < 0) return VSA_ERR_INVALID_ARG;
   if (gl == 0) std::memcpy(p.latent_k, p.latent, sizeof(p.latent));
   if (gc == 0) std::memcpy(p.cube_k, p.cube, sizeof(p.cube));
+  const int64_t nq_tok = (int64_t)p.prefix_len + (int64_t)p.latent[0] * p.latent[1] * p.latent[2];
+  const int64_t nk_tok = (int64_t)p.prefix_len + (int64_t)p.latent_k[0] * p.latent_k[1] * p.latent_k[2];
+  if (gq == 0) {
+    p.stride_n = p.head_dim;
+    p.stride_h = nq_tok * p.head_dim;
+    p.stride_b = (int64_t)p.heads * nq_tok * p.head_dim;
+  }
+  if (go == 0) {
+    p.o_stride_b = p.stride_b;
+    p.o_stride_h = p.stride_h;
+    p.o_stride_n = p.stride_n;
+  }
   if (gs == 0) {
-    p.kv_stride_b = p.stride_b;
-    p.kv_stride_h = p.stride_h;
-    p.kv_stride_n = p.stride_n;
+    const bool same_grid = std::memcmp(p.latent_k, p.latent, sizeof(p.latent)) == 0;
+    p.kv_stride_n = same_grid ? p.stride_n : p.head_dim;
+    p.kv_stride_h = same_grid ? p.stride_h : nk_tok * p.head_dim;
+    p.kv_stride_b = same_grid ? p.stride_b : (int64_t)p.heads * nk_tok * p.head_dim;
   }
   if (p.dtype != VSA_DTYPE_BF16 && p.dtype != VSA_DTYPE_F16) return VSA_ERR_UNSUPPORTED;
   if (p.head_dim != 64 && p.head_dim != 128) return VSA_ERR_UNSUPPORTED;
@@ -190,11 +206,44 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
 
 extern "C" int vsa_topk_for_sparsity(int32_t num_blocks, double sparsity) {
   if (num_blocks < 1 || !(sparsity >= 0.0 && sparsity < 1.0)) return VSA_ERR_INVALID_ARG;
-  // the 1e-9 absorbs the rounding of 1 - s (e.g. 120 * (1 - 0.9))
-  const double keep = std::floor((double)num_blocks * (1.0 - sparsity) + 0.5 + 1e-9);
+  // floor(nb * (1 - s)); a product within 1e-9 (relative) of an integer is
+  // that integer, since decimal sparsities are not exact in binary (e.g.
+  // 120 * (1 - 0.9) evaluates to 11.999999999999998)
+  const double x = (double)num_blocks * (1.0 - sparsity);
+  const double n = std::nearbyint(x);
+  const double keep = std::fabs(x - n) <= 1e-9 * std::fmax(1.0, x) ? n : std::floor(x);
   if (keep < 1.0) return 1;
   if (keep > (double)num_blocks) return num_blocks;
   return (int)keep;
+}
+
+extern "C" int vsa_block_counts(const vsa_plan_t* plan, int32_t side, int32_t* counts, int64_t len) {
+  if (plan == nullptr || (side != VSA_SIDE_Q && side != VSA_SIDE_K) || len < 0 || (counts == nullptr && len > 0))
+    return VSA_ERR_INVALID_ARG;
+  const vsa_problem& p = plan->p;
+  const int32_t* latent = side == VSA_SIDE_Q ? p.latent : p.latent_k;
+  const int32_t* cube = side == VSA_SIDE_Q ? p.cube : p.cube_k;
+  Side g;
+  const int st = derive_side(latent, cube, p.prefix_len, g);
+  if (st != VSA_OK) return st;
+  const int64_t total = g.Pb + g.nb;
+  if (counts != nullptr) {
+    int64_t i = 0;
+    // prefix blocks: V tokens each, the last one the remainder
+    for (int64_t b = 0; b < g.Pb && i < len; ++b, ++i) {
+      const int64_t rest = (int64_t)p.prefix_len - b * g.V;
+      counts[i] = (int32_t)(rest < g.V ? rest : g.V);
+    }
+    // cubes in raster order of the cube grid: the product over the axes of
+    // the cube's extent clipped to the grid
+    for (int64_t c = 0; c < g.nb && i < len; ++c, ++i) {
+      const int64_t bw = c % g.nW, bh = (c / g.nW) % g.nH, bt = c / (g.nW * g.nH);
+      const int64_t et = std::min(g.ct, g.T - bt * g.ct), eh = std::min(g.ch, g.H - bh * g.ch),
+                    ew = std::min(g.cw, g.W - bw * g.cw);
+      counts[i] = (int32_t)(et * eh * ew);
+    }
+  }
+  return (int)total;
 }
 
 extern "C" int vsa_describe(const vsa_plan_t* plan, char* buf, size_t len) {

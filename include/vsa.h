@@ -95,9 +95,12 @@ typedef struct vsa_problem {
   int32_t topk;           /* cubes kept per query block, 1..num_blocks       */
   int32_t prefix_len;     /* P >= 0 tokens before the grid, always kept      */
   int32_t dtype;          /* VSA_DTYPE_BF16 or VSA_DTYPE_F16                 */
-  int64_t stride_b, stride_h, stride_n;        /* q strides (elements); k and
-                                                  v too unless kv_stride_* set */
-  int64_t o_stride_b, o_stride_h, o_stride_n;  /* o strides (elements)       */
+  int64_t stride_b, stride_h, stride_n;        /* q strides (elements), all
+                                                  >= 1, or all 0: contiguous
+                                                  [B][Hh][N][D]; k and v too
+                                                  unless kv_stride_* set      */
+  int64_t o_stride_b, o_stride_h, o_stride_n;  /* o strides (elements), or all
+                                                  0: the same as q's          */
   /* k and v on a grid of their own (fastbsa package page, section "Use":
      latent_shape_k and chunk_3d_shape_k next to q's shapes). Each group
      all zero means "same as q". Query blocks then come from (latent, cube),
@@ -105,11 +108,12 @@ typedef struct vsa_problem {
      both sequences, each side cutting its prefix by its own cube volume. */
   int32_t latent_k[3];    /* (T, H, W) of k and v, each >= 1, or all 0      */
   int32_t cube_k[3];      /* key cube shape, each >= 1, or all 0            */
-  int64_t kv_stride_b, kv_stride_h, kv_stride_n;  /* k, v strides, or all 0 */
+  int64_t kv_stride_b, kv_stride_h, kv_stride_n;  /* k, v strides, or all 0:
+                             q's on q's grid, else contiguous [B][Hh][N_k][D] */
 } vsa_problem;
 
 /* Derived geometry; filled by vsa_plan, plain data, owned by the caller.
-   p holds the problem with the key-side groups filled in (never zero). */
+   p holds the problem with every defaulted group filled in (never zero). */
 typedef struct vsa_plan_t {
   vsa_problem p;
   int32_t nblk[3];            /* query cubes per axis: ceil(T/ct), ceil(H/ch), ceil(W/cw) */
@@ -140,10 +144,12 @@ typedef struct vsa_plan_t {
 int vsa_plan(const vsa_problem* problem, vsa_plan_t* out);
 
 /* Top-k for a sparsity s in [0, 1), the fraction of key cubes dropped
- * (fastbsa package page, section "Use": sparsity=0.9375 keeps 1/16): the
- * nearest integer to num_blocks * (1 - s), halves rounded up, clamped to
- * 1..num_blocks. Returns it, or VSA_ERR_INVALID_ARG for num_blocks < 1 or
- * s outside [0, 1) (NaN included). Host only. */
+ * (fastbsa package page, section "Use": sparsity=0.9375 keeps 1/16):
+ * floor(num_blocks * (1 - s)), at least 1, so the kept fraction never
+ * exceeds 1 - s; a product within 1e-9 (relative) of an integer counts as
+ * that integer (decimal sparsities are not exact in binary). Returns it, or
+ * VSA_ERR_INVALID_ARG for num_blocks < 1 or s outside [0, 1) (NaN
+ * included). Host only. */
 int vsa_topk_for_sparsity(int32_t num_blocks, double sparsity);
 
 /* Block selection (pages: user guide opening definition; fastbsa "How it
@@ -155,6 +161,16 @@ int vsa_topk_for_sparsity(int32_t num_blocks, double sparsity);
  * plan->sel_elems. stream: hipStream_t or NULL. Asynchronous. */
 int vsa_select(const vsa_plan_t* plan, const void* q, const void* k,
                void* workspace, int32_t* sel, void* stream);
+
+/* The two steps of vsa_select, for callers that time them apart or reuse
+ * the pooled means. vsa_pool writes qbar and kbar into the workspace (same
+ * arguments and rules as vsa_select); vsa_score_topk reads them from the
+ * workspace and writes sel. vsa_select is vsa_pool then vsa_score_topk on
+ * the same stream. Asynchronous. */
+int vsa_pool(const vsa_plan_t* plan, const void* q, const void* k,
+             void* workspace, void* stream);
+int vsa_score_topk(const vsa_plan_t* plan, const void* workspace,
+                   int32_t* sel, void* stream);
 
 /* Block-sparse attention (pages: user guide opening definition; fastbsa
  * "How it works": raster-to-block index map evaluated inside the kernel).
@@ -171,6 +187,22 @@ int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k,
 int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k,
                 const void* v, void* workspace, int32_t* sel, void* o,
                 void* stream);
+
+/* Grid sides for vsa_block_counts. */
+enum { VSA_SIDE_Q = 0, VSA_SIDE_K = 1 };
+
+/* Valid token count of every block of one side's grid, in block-id order:
+ * the prefix blocks (V tokens each, the last one the remainder of the
+ * prefix), then the cubes in raster order of the cube grid (a cube at the
+ * far edge of an axis holds only the tokens inside the grid). side
+ * VSA_SIDE_Q: q's grid (num_q_blocks entries); VSA_SIDE_K: the key grid
+ * (num_prefix_blocks_k + num_blocks entries). Writes min(len, count)
+ * entries to counts (host memory, caller-owned; may be NULL when len is 0)
+ * and returns the count, or VSA_ERR_INVALID_ARG (null plan, unknown side,
+ * len < 0) or vsa_plan's error for a plan that is not valid. Host only
+ * (user guide, "Wan top-k behavior": 120 cubes for the (31, 22, 40) grid
+ * in (4, 8, 8) blocks, the edge cubes partial). */
+int vsa_block_counts(const vsa_plan_t* plan, int32_t side, int32_t* counts, int64_t len);
 
 /* Formats the routing fields of the user guide's Wan log line
  * ("seq_len=..., dit_seq_shape=(T, H, W), block_size=(ct, ch, cw),

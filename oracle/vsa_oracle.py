@@ -40,13 +40,17 @@ notes with its reason):
       chunk_3d_shape_k). Query blocks come from q's grid and cubes, key
       blocks from k's; the prefix length is the same for both sequences and
       each side cuts its prefix by its own cube volume;
-  R21 sparsity s (fastbsa "Use") keeps round(nb * (1 - s)) key cubes, ties
-      rounded up, clamped to 1..nb.
+  R21 sparsity s (fastbsa "Use") keeps floor(nb * (1 - s)) key cubes, at
+      least one (the kept fraction never exceeds 1 - s); a product within
+      1e-9 of an integer counts as that integer, since decimal sparsities
+      such as 0.9 are not exact in binary.
 
-Parity pins: every function here is pinned by tests in
-``tests/test_oracle_pins.py`` against closed forms, the pages' numbers,
-library routines (torch scaled_dot_product_attention in float64) and an
-independent per-token brute force. No function is unpinned.
+Parity pins: every function here, the comparison helpers included, is
+pinned by tests in ``tests/test_oracle_pins.py`` against closed forms, the
+pages' numbers, exact rational arithmetic, library routines (torch
+scaled_dot_product_attention in float64) and an independent per-token brute
+force; ``test_planted_mistakes`` shows that a plausible slip in each is
+caught.
 """
 from __future__ import annotations
 
@@ -166,12 +170,15 @@ def routing_summary(g: Geometry, topk: int) -> dict:
 
 
 def topk_for_sparsity(num_blocks: int, sparsity: float) -> int:
-    """Key cubes kept for a sparsity s in [0, 1) (fastbsa "Use"; R21): the
-    nearest integer to nb * (1 - s), halves rounded up, at least 1."""
+    """Key cubes kept for a sparsity s in [0, 1) (fastbsa "Use": 0.9375
+    keeps 1/16; R21): floor(nb * (1 - s)), at least 1. A product within
+    1e-9 (relative) of an integer is that integer."""
     s = float(sparsity)
     if not (0.0 <= s < 1.0):
         raise ValueError("sparsity must be in [0, 1)")
-    keep = math.floor(num_blocks * (1.0 - s) + 0.5 + 1e-9)
+    x = num_blocks * (1.0 - s)
+    n = round(x)
+    keep = n if abs(x - n) <= 1e-9 * max(1.0, x) else math.floor(x)
     return int(min(max(keep, 1), num_blocks))
 
 
@@ -384,9 +391,28 @@ def check_selection(sel: np.ndarray, scores: np.ndarray, topk: int,
 
 
 def error_norms(out: np.ndarray, ref: np.ndarray) -> dict:
-    """Max-abs and relative L2 error of ``out`` against ``ref`` (float64)."""
+    """Error of ``out`` against the reference ``ref`` (same shape), in
+    float64: max_abs = max |out - ref| over all elements, rel_l2 =
+    ||out - ref||_2 / ||ref||_2 (Frobenius norms over all elements). A zero
+    reference gives rel_l2 0 when out is zero too, else infinity. Empty
+    inputs give zeros."""
     o = np.asarray(out, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
+    if o.shape != r.shape:
+        raise ValueError(f"shape mismatch {o.shape} vs {r.shape}")
+    if o.size == 0:
+        return {"max_abs": 0.0, "rel_l2": 0.0}
     diff = o - r
-    return {"max_abs": float(np.max(np.abs(diff))) if diff.size else 0.0,
-            "rel_l2": float(np.linalg.norm(diff) / max(np.linalg.norm(r), 1e-300))}
+    nd, nr = float(np.linalg.norm(diff)), float(np.linalg.norm(r))
+    rel = nd / nr if nr > 0.0 else (0.0 if nd == 0.0 else math.inf)
+    return {"max_abs": float(np.max(np.abs(diff))), "rel_l2": rel}
+
+
+def error_norms_by_block(out: np.ndarray, ref: np.ndarray, g: Geometry,
+                         blocks: Optional[Iterable[int]] = None) -> dict:
+    """error_norms of the rows of each query block of ``g`` on its own
+    (out, ref: [N, D] of one (batch, head)), so that an error confined to
+    a few blocks is not averaged away. Returns {block id: norms} for the
+    given blocks (default all)."""
+    ids = range(g.num_q_blocks) if blocks is None else blocks
+    return {int(i): error_norms(np.asarray(out)[g.members[i]], np.asarray(ref)[g.members[i]]) for i in ids}

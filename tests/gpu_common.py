@@ -86,6 +86,8 @@ def check_outputs(w, g, res, heads, blocks_per_head=None, rng_seed=0):
         got = res["out"][b, h][rows]
         assert np.all(np.isfinite(got)), "non-finite GPU output"
         e = O.error_norms(got, ref[rows])
+        per = O.error_norms_by_block(res["out"][b, h], ref, g, blocks)
         worst["max_abs"] = max(worst["max_abs"], e["max_abs"])
         worst["rel_l2"] = max(worst["rel_l2"], e["rel_l2"])
+        worst["block_rel_l2"] = max(worst.get("block_rel_l2", 0.0), max(x["rel_l2"] for x in per.values()))
     return worst

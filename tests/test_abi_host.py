@@ -42,7 +42,7 @@ def test_struct_layout_matches_c(tmp_path):
              'printf("%zu %zu\\n", sizeof(vsa_problem), sizeof(vsa_plan_t));']
     lines += [f'printf("p {f} %zu\\n", offsetof(vsa_problem, {f}));' for f in fields_p]
     lines += [f'printf("l {f} %zu\\n", offsetof(vsa_plan_t, {f}));' for f in fields_l]
-    consts = [n for n in dir(_lib) if re.fullmatch(r"VSA_(DTYPE|ERR)_\w+|VSA_OK", n)]
+    consts = [n for n in dir(_lib) if re.fullmatch(r"VSA_(DTYPE|ERR|SIDE)_\w+|VSA_OK", n)]
     lines += [f'printf("c {n} %d\\n", (int){n});' for n in consts]
     lines.append("return 0;}")
     c = tmp_path / "layout.c"
@@ -89,6 +89,51 @@ def test_plan_geometry_matches_oracle(latent, cube, prefix):
     assert (pl.num_blocks, pl.num_prefix_blocks, pl.num_q_blocks, pl.seq_len) == \
         (g.num_blocks, g.num_prefix_blocks, g.num_q_blocks, g.seq_len)
     assert np.array_equal(pl.valid_counts(), g.counts)
+
+
+@pytest.mark.parametrize("lq,cq,lk,ck,prefix", [
+    ((4, 10, 12), (4, 4, 4), (8, 10, 12), (4, 4, 4), 0),
+    ((5, 7, 9), (3, 4, 5), (6, 5, 8), (2, 3, 3), 9),
+    ((5, 9, 17), (4, 8, 8), (7, 6, 9), (2, 4, 4), 100),
+])
+def test_block_counts_of_both_grids_match_oracle(lq, cq, lk, ck, prefix):
+    pl = vsa.plan(1, 2, 128, lq, cq, 1, prefix, latent_k=lk, cube_k=ck)
+    assert np.array_equal(pl.valid_counts("q"), O.geometry(lq, cq, prefix).counts)
+    gk = O.geometry(lk, ck, prefix)
+    assert np.array_equal(pl.valid_counts("k"), gk.counts)
+    assert pl.num_prefix_blocks_k + pl.num_blocks == gk.num_q_blocks
+
+
+def test_block_counts_argument_handling():
+    pl = vsa.plan(1, 2, 128, (5, 6, 7), (2, 4, 4), 3, 20)
+    L = _lib.lib()
+    n = L.vsa_block_counts(ctypes.byref(pl.raw), _lib.VSA_SIDE_Q, None, 0)
+    assert n == pl.num_q_blocks
+    buf = (ctypes.c_int32 * 4)(-7, -7, -7, -7)
+    assert L.vsa_block_counts(ctypes.byref(pl.raw), _lib.VSA_SIDE_Q, buf, 3) == n   # writes 3
+    assert list(buf) == list(O.geometry((5, 6, 7), (2, 4, 4), 20).counts[:3]) + [-7]
+    assert L.vsa_block_counts(None, 0, None, 0) == _lib.VSA_ERR_INVALID_ARG
+    assert L.vsa_block_counts(ctypes.byref(pl.raw), 2, None, 0) == _lib.VSA_ERR_INVALID_ARG
+    assert L.vsa_block_counts(ctypes.byref(pl.raw), 0, None, -1) == _lib.VSA_ERR_INVALID_ARG
+    assert L.vsa_block_counts(ctypes.byref(pl.raw), 0, None, 5) == _lib.VSA_ERR_INVALID_ARG
+
+
+def test_plan_default_strides():
+    """All-zero stride groups take the documented defaults: q contiguous,
+    o like q, k and v like q on q's grid and contiguous on their own."""
+    B, Hh, D, P = 2, 3, 64, 20
+    pl = vsa.plan(B, Hh, D, (5, 6, 7), (2, 4, 4), 3, P)
+    N = P + 5 * 6 * 7
+    assert (pl.stride_b, pl.stride_h, pl.stride_n) == (Hh * N * D, N * D, D)
+    assert (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n) == (Hh * N * D, N * D, D)
+    assert pl.kv_strides == (Hh * N * D, N * D, D)
+    custom = (Hh * N * 2 * D, 2 * D, Hh * 2 * D)          # a [B, N, Hh, 2D] view
+    pl = vsa.plan(B, Hh, D, (5, 6, 7), (2, 4, 4), 3, P, strides=custom)
+    assert (pl.o_stride_b, pl.o_stride_h, pl.o_stride_n) == custom and pl.kv_strides == custom
+    pl = vsa.plan(B, Hh, D, (5, 6, 7), (2, 4, 4), 3, P, strides=custom, latent_k=(8, 6, 7))
+    Nk = P + 8 * 6 * 7
+    assert pl.kv_strides == (Hh * Nk * D, Nk * D, D) and pl.seq_len_k == Nk
+    assert _status(o_strides=(0, 0, 64)) == _lib.VSA_ERR_INVALID_ARG
 
 
 def _status(**kw):

@@ -50,9 +50,11 @@ def _full_check(w, topk, heads=None, blocks_per_head=None, dtype="bf16"):
         heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
     worst = G.check_outputs(w, g, res, heads, blocks_per_head)
     _announce(f"{w.name}/topk{topk}/{dtype}: band rows {chk['band_rows']} of {chk['rows']}, "
-              f"max_abs {worst['max_abs']:.3e} rel_l2 {worst['rel_l2']:.3e}")
+              f"max_abs {worst['max_abs']:.3e} rel_l2 {worst['rel_l2']:.3e} "
+              f"per block <= {worst['block_rel_l2']:.3e}")
     assert worst["max_abs"] <= G.TOL[dtype]["max_abs"]
     assert worst["rel_l2"] <= G.TOL[dtype]["rel_l2"]
+    assert worst["block_rel_l2"] <= G.TOL[dtype]["rel_l2"]
     return res, g
 
 
@@ -87,6 +89,10 @@ SMALL = [
     # 36 query blocks over 8 XCD ranges of 5: the last range holds one unit,
     # every unit runs as two half-row workgroups
     ("units_uneven_xcd", 1, 3, 128, (9, 10, 11), (4, 8, 8), 5, 0),
+    # odd cube volumes (slot tables of an odd entry count): 27 tokens (the
+    # 2-wave tiling) and 125 tokens (the 8-wave tiling), with a prefix
+    ("odd_cube_v27", 1, 2, 128, (7, 8, 9), (3, 3, 3), 5, 11),
+    ("odd_cube_v125", 1, 2, 128, (9, 11, 12), (5, 5, 5), 4, 13),
 ]
 
 
@@ -337,6 +343,9 @@ CROSS = [
     ("cross_prefix", 2, 2, 64, (3, 6, 7), (2, 4, 4), (5, 5, 9), (4, 4, 4), 4, 40),
     ("cross_odd_shapes", 1, 2, 128, (5, 7, 9), (3, 4, 5), (6, 5, 8), (2, 3, 3), 5, 9),
     ("cross_q256_kprefix", 1, 2, 128, (5, 9, 17), (4, 8, 8), (7, 6, 9), (2, 4, 4), 4, 100),
+    # 4096 one-token key cubes, all kept: the kept-block table (32 KB) leaves
+    # no room for four K/V stages, so the 8-wave tiling runs rings of two
+    ("cross_kept_table_fills_lds", 1, 1, 128, (4, 8, 8), (4, 8, 8), (4, 32, 32), (1, 1, 1), 4096, 0),
 ]
 
 

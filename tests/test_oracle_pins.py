@@ -339,17 +339,33 @@ def test_one_token_query_blocks_score_each_token():
 
 def test_topk_for_sparsity():
     """fastbsa "Use" passes sparsity 0.9375: 1/16 of the cubes are kept
-    (R21: nearest integer, halves up, at least one, at most all)."""
-    assert O.topk_for_sparsity(960, 0.9375) == 60
+    (R21: floor(nb * (1 - s)), at least one, at most all)."""
+    g = _golden("block_shapes.json")
+    assert O.topk_for_sparsity(960, g["fastbsa_sparsity"]) == 60     # the page's 1/16 of 960
     assert O.topk_for_sparsity(624, 0.9375) == 39
-    assert O.topk_for_sparsity(120, 0.9375) == 8        # 7.5 rounds up
-    assert O.topk_for_sparsity(120, 0.9) == 12          # 12 up to float rounding of 1 - 0.9
+    assert O.topk_for_sparsity(120, 0.9375) == 7        # 7.5: the kept fraction stays <= 1/16
+    assert O.topk_for_sparsity(1320, 0.9375) == 82      # 82.5
+    assert O.topk_for_sparsity(120, 0.9) == 12          # 120 * (1 - 0.9) = 11.999999999999998 in binary
     assert O.topk_for_sparsity(120, 0.0) == 120
     assert O.topk_for_sparsity(120, 0.999) == 1         # 0.12 -> at least one
-    assert O.topk_for_sparsity(7, 0.5) == 4             # 3.5 rounds up
+    assert O.topk_for_sparsity(7, 0.5) == 3             # 3.5
     for bad in (-0.1, 1.0, float("nan")):
         with pytest.raises(ValueError):
             O.topk_for_sparsity(120, bad)
+
+
+def test_topk_for_sparsity_exact_rationals():
+    """Against exact rational arithmetic: for every block count up to 4096
+    and the sparsities a/16 (exact in binary) and a/100 (decimal, inexact in
+    binary), the kept count is max(1, floor(nb * (1 - s))) computed with
+    fractions.Fraction."""
+    from fractions import Fraction
+    for den, nums in ((16, range(16)), (100, (0, 1, 10, 25, 50, 75, 80, 90, 95, 99))):
+        for a in nums:
+            s = Fraction(a, den)
+            for nb in list(range(1, 257)) + [600, 624, 960, 1000, 1320, 2048, 4095, 4096]:
+                want = max(1, int(nb * (1 - s)))        # int() of a positive Fraction is floor
+                assert O.topk_for_sparsity(nb, a / den) == want, (nb, a, den)
 
 
 def test_shift_of_all_keys_changes_nothing():
@@ -400,6 +416,51 @@ def test_decode_f16_matches_numpy_on_every_pattern():
 
 
 # ----------------------------------------------------------------------------
+# comparison helpers (fastbsa "How it works": outputs are validated against
+# dense-masked attention; these norms make that call)
+# ----------------------------------------------------------------------------
+
+def test_error_norms_closed_forms():
+    rng = np.random.default_rng(41)
+    ref = rng.standard_normal((37, 16))
+    # out = ref + d * e_i: max_abs is exactly |d|, rel_l2 is |d| / ||ref||
+    for d in (0.25, -0.125):
+        out = ref.copy()
+        out[5, 3] += d
+        e = O.error_norms(out, ref)
+        assert e["max_abs"] == abs(d)
+        assert e["rel_l2"] == pytest.approx(abs(d) / math.sqrt(float(np.sum(ref * ref))), rel=1e-12)
+    # out = 2 ref: rel_l2 1 (normalised by the reference, not by out)
+    assert O.error_norms(2.0 * ref, ref)["rel_l2"] == pytest.approx(1.0, rel=1e-14)
+    # out = -ref: rel_l2 2; out = ref: zeros
+    assert O.error_norms(-ref, ref)["rel_l2"] == pytest.approx(2.0, rel=1e-14)
+    assert O.error_norms(ref, ref) == {"max_abs": 0.0, "rel_l2": 0.0}
+    # a zero reference is guarded: 0 for a zero output, infinity otherwise
+    z = np.zeros((3, 4))
+    assert O.error_norms(z, z) == {"max_abs": 0.0, "rel_l2": 0.0}
+    assert O.error_norms(z + 1.0, z)["rel_l2"] == math.inf
+    assert O.error_norms(np.zeros((0, 4)), np.zeros((0, 4))) == {"max_abs": 0.0, "rel_l2": 0.0}
+    with pytest.raises(ValueError):
+        O.error_norms(z, np.zeros((4, 3)))
+
+
+def test_error_norms_by_block_localises_an_error():
+    """An error confined to one block shows up in that block's own norms at
+    full size while the whole-tensor relative L2 stays small."""
+    g = O.geometry((5, 6, 7), (2, 4, 4), 7)
+    ref = np.random.default_rng(43).standard_normal((g.seq_len, 8))
+    out = ref.copy()
+    bad = 5
+    out[g.members[bad]] *= 1.5
+    per = O.error_norms_by_block(out, ref, g)
+    assert set(per) == set(range(g.num_q_blocks))
+    assert per[bad]["rel_l2"] == pytest.approx(0.5, rel=1e-12)
+    assert all(per[i]["rel_l2"] == 0.0 for i in per if i != bad)
+    assert O.error_norms(out, ref)["rel_l2"] < 0.5
+    assert O.error_norms_by_block(out, ref, g, blocks=[bad, 0]).keys() == {bad, 0}
+
+
+# ----------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ----------------------------------------------------------------------------
 
@@ -445,9 +506,26 @@ def _attend_query_prefix_count(q, k, v, sel, g, query_blocks=None, return_rowsum
     return out
 
 
-def _sparsity_floor(num_blocks, sparsity):
-    # truncation instead of rounding
-    return max(1, int(num_blocks * (1.0 - sparsity)))
+def _sparsity_nearest(num_blocks, sparsity):
+    # nearest integer, halves up, instead of floor
+    return int(min(max(math.floor(num_blocks * (1.0 - sparsity) + 0.5 + 1e-9), 1), num_blocks))
+
+
+def _sparsity_plain_floor(num_blocks, sparsity):
+    # floor of the binary product, with no allowance for decimal sparsities
+    return int(min(max(math.floor(num_blocks * (1.0 - sparsity)), 1), num_blocks))
+
+
+def _norms_by_out(out, ref):
+    # normalised by the output instead of the reference
+    d = np.asarray(out, dtype=np.float64) - np.asarray(ref, dtype=np.float64)
+    return {"max_abs": float(np.max(np.abs(d))), "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(out))}
+
+
+def _norms_signed_max(out, ref):
+    # signed maximum of the difference instead of the maximum magnitude
+    d = np.asarray(out, dtype=np.float64) - np.asarray(ref, dtype=np.float64)
+    return {"max_abs": float(np.max(d)), "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref))}
 
 
 def _f16_bias_16(bits):
@@ -466,7 +544,10 @@ def _f16_subnormals_as_normals(bits):
 
 @pytest.mark.parametrize("target,mutant,pin", [
     ("attend_dense_masked", _attend_query_prefix_count, "brute_cross_prefix"),
-    ("topk_for_sparsity", _sparsity_floor, "sparsity"),
+    ("topk_for_sparsity", _sparsity_nearest, "sparsity"),
+    ("topk_for_sparsity", _sparsity_plain_floor, "sparsity_exact"),
+    ("error_norms", _norms_by_out, "norms"),
+    ("error_norms", _norms_signed_max, "norms"),
     ("decode_f16", _f16_bias_16, "f16_closed"),
     ("decode_f16", _f16_subnormals_as_normals, "f16_numpy"),
     ("pool", _pool_zero_padded, "centroid"),
@@ -487,6 +568,8 @@ def test_planted_mistakes(monkeypatch, target, mutant, pin):
         "sdpa": lambda: test_all_blocks_equals_dense_sdpa((5, 6, 7), (2, 4, 4), 0, 32),
         "brute_cross_prefix": lambda: test_brute_force_cross_grids(*CROSS_CASES[1]),
         "sparsity": test_topk_for_sparsity,
+        "sparsity_exact": test_topk_for_sparsity_exact_rationals,
+        "norms": test_error_norms_closed_forms,
         "f16_closed": test_decode_f16_exact,
         "f16_numpy": test_decode_f16_matches_numpy_on_every_pattern,
     }
