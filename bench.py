@@ -222,6 +222,39 @@ def _phase_stats(ms, flops, pl, peak):
     }
 
 
+def _short_kernel(name: str) -> str:
+    """A kernel's plain name (vsa_attend_kernel, ...) from a demangled or
+    mangled symbol."""
+    import re
+    m = re.search(r"(vsa_\w+?_kernel|__amd_\w+)", name)
+    return m.group(1) if m else name[:60]
+
+
+def summarize_trace(path: str, skip: int) -> str:
+    """Per-kernel dispatch statistics of a rocprofv3 kernel-trace CSV,
+    dropping the first ``skip`` dispatches of each kernel (the warm-up
+    steps), in microseconds."""
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            rows.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), dur))
+    lines = [f"{'kernel':<28}{'calls':>6}{'avg_us':>11}{'median_us':>11}{'min_us':>11}{'max_us':>11}"]
+    total = {}
+    for name, xs in rows.items():
+        xs.sort()
+        d = np.array([x[1] for x in xs[skip:]]) if len(xs) > skip else np.array([])
+        if d.size:
+            total[name] = d
+    grand = sum(d.sum() for d in total.values())
+    for name, d in sorted(total.items(), key=lambda kv: -kv[1].sum()):
+        lines.append(f"{_short_kernel(name):<28}{d.size:>6}{d.mean():>11.1f}{np.median(d):>11.1f}"
+                     f"{d.min():>11.1f}{d.max():>11.1f}   {100.0 * d.sum() / grand:5.2f}%")
+    lines.append(f"(first {skip} dispatches of each kernel dropped)")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,8 +271,14 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="only print per-kernel statistics of a rocprofv3 kernel-trace CSV")
+    ap.add_argument("--skip", type=int, default=0, help="with --summarize-trace: warm-up dispatches to drop")
     args = ap.parse_args(argv)
 
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.skip))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path shards over (batch, head) with no exchange "
               "inside attention, and multi-GPU runs are not part of this build. Use --gpus 1.",

@@ -80,16 +80,41 @@ class VsaError(RuntimeError):
 _lib = None
 
 
+def hip_runtimes_mapped() -> set:
+    """Distinct HIP runtime files (libamdhip64) mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {os.path.realpath(line.split()[-1]) for line in f if "libamdhip64" in line}
+    except OSError:  # pragma: no cover - not Linux
+        return set()
+
+
 def lib() -> ctypes.CDLL:
     """Load libvsa.so once. Raises if it has not been built: there is no
-    fallback path."""
+    fallback path.
+
+    The library must share PyTorch's HIP runtime (PyTorch owns the device
+    memory and streams it is given). PyTorch ships its own copy of the
+    runtime, so torch is imported first: the library's dependency then
+    resolves to the copy already loaded. Loaded the other way round, the
+    process would hold two runtimes, and the library's would not see the
+    memory or the device that torch's set up; that state raises here."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing; build it with "
                 "`python -m block_sparse_attention_raster_amd.build` (hipcc, gfx950)")
+        try:
+            import torch  # noqa: F401  (loads torch's HIP runtime before this library)
+        except ImportError:  # pragma: no cover - the binding is used with torch
+            pass
         L = ctypes.CDLL(LIB_PATH)
+        runtimes = hip_runtimes_mapped()
+        if len(runtimes) > 1:
+            raise RuntimeError(
+                "two HIP runtimes are loaded in this process (" + ", ".join(sorted(runtimes)) + "): "
+                f"{LIB_PATH} must use the one torch uses; import torch before loading it")
         vp = ctypes.c_void_p
         L.vsa_plan.argtypes = [ctypes.POINTER(VsaProblem), ctypes.POINTER(VsaPlan)]
         L.vsa_plan.restype = ctypes.c_int

@@ -7,6 +7,7 @@ import json
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -347,3 +348,21 @@ def test_route_unsupported_and_errors():
     assert L.vsa_route(ctypes.byref(pr), 5, ctypes.byref(out)) == _lib.VSA_ERR_INVALID_ARG
     assert L.vsa_route(None, 0, ctypes.byref(out)) == _lib.VSA_ERR_INVALID_ARG
     assert L.vsa_describe_route(None, None, 0) == _lib.VSA_ERR_INVALID_ARG
+
+
+def test_library_binds_to_the_hip_runtime_torch_uses():
+    """Loading the library before torch was ever imported (here in a fresh
+    process whose first act is a host-only call) still leaves a single HIP
+    runtime in the process: the one torch ships, so that the library sees
+    torch's device memory and streams."""
+    code = ("import sys; sys.path.insert(0, sys.argv[1])\n"
+            "import block_sparse_attention_raster_amd as vsa\n"
+            "from block_sparse_attention_raster_amd import _lib\n"
+            "vsa.plan(1, 2, 128, (5, 6, 7), (2, 4, 4), 3)\n"
+            "import torch, os\n"
+            "rt = _lib.hip_runtimes_mapped()\n"
+            "assert len(rt) == 1, rt\n"
+            "assert os.path.dirname(next(iter(rt))) == os.path.realpath(os.path.join(os.path.dirname(torch.__file__), 'lib')), rt\n"
+            "print('one runtime')\n")
+    r = subprocess.run([sys.executable, "-c", code, ROOT], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "one runtime" in r.stdout, (r.stdout[-2000:], r.stderr[-2000:])
