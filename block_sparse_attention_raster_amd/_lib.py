@@ -15,6 +15,7 @@ VSA_ERR_ALIGN = -4
 VSA_ERR_OVERFLOW = -5
 VSA_ERR_DEVICE = -6
 VSA_ERR_LAUNCH = -7
+VSA_ERR_SCRATCH = -8
 VSA_DTYPE_BF16 = 0
 VSA_DTYPE_F16 = 1
 VSA_SIDE_Q = 0
@@ -22,7 +23,7 @@ VSA_SIDE_K = 1
 
 EXPORTED = ("vsa_plan", "vsa_topk_for_sparsity", "vsa_select", "vsa_attend", "vsa_forward",
             "vsa_describe", "vsa_status_str", "vsa_route", "vsa_describe_route", "vsa_block_counts",
-            "vsa_pool", "vsa_score_topk")
+            "vsa_pool", "vsa_score_topk", "vsa_forward_noalloc")
 
 VSA_ROUTE_VSA = 0
 VSA_ROUTE_VSA_ALL_BLOCKS = 1
@@ -130,6 +131,8 @@ def lib() -> ctypes.CDLL:
         L.vsa_attend.restype = ctypes.c_int
         L.vsa_forward.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp, vp, vp]
         L.vsa_forward.restype = ctypes.c_int
+        L.vsa_forward_noalloc.argtypes = [ctypes.POINTER(VsaPlan), vp, vp, vp, vp, vp, vp]
+        L.vsa_forward_noalloc.restype = ctypes.c_int
         L.vsa_describe.argtypes = [ctypes.POINTER(VsaPlan), ctypes.c_char_p, ctypes.c_size_t]
         L.vsa_describe.restype = ctypes.c_int
         L.vsa_route.argtypes = [ctypes.POINTER(VsaProblem), ctypes.c_int32, ctypes.POINTER(VsaRoute)]

@@ -16,6 +16,13 @@ hipError_t vsa_launch_score_topk(const VsaArgs& a, const float* qbar, const floa
 hipError_t vsa_launch_attend(const VsaArgs& a, int variant, const void* q, const void* k, const void* v,
                              const int32_t* sel, void* o, hipStream_t stream);
 
+// Scratch memory of vsa_forward_noalloc: the pooled means (qbar, kbar) in a
+// fixed device array, so that the call allocates nothing. Each device holds
+// its own copy from the library's load until the process ends. In host code
+// `scratch` names a host-side stand-in, never device memory: the device
+// address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[VSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -178,4 +185,43 @@ extern "C" int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k,
   const int st = vsa_select(plan, q, k, workspace, sel, stream);
   if (st != VSA_OK) return st;
   return vsa_attend(plan, q, k, v, sel, o, stream);
+}
+
+namespace {
+
+// Device address of `scratch` on each device, looked up once per device
+// with that device current (0: not yet).
+std::atomic<uintptr_t> g_scratch[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VSA_ERR_DEVICE;
+  uintptr_t p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();   // leave no error behind for the caller's next HIP call
+      return VSA_ERR_DEVICE;
+    }
+    p = reinterpret_cast<uintptr_t>(ptr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = reinterpret_cast<void*>(p);
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" int vsa_forward_noalloc(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+                                   int32_t* sel, void* o, void* stream) {
+  int st = check_plan(plan);
+  if (st != VSA_OK) return st;
+  if (plan->workspace_bytes > (int64_t)VSA_NOALLOC_SCRATCH_BYTES) return VSA_ERR_SCRATCH;
+  if (q == nullptr || k == nullptr || v == nullptr || sel == nullptr || o == nullptr) return VSA_ERR_INVALID_ARG;
+  if ((st = check_device()) != VSA_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != VSA_OK) return st;
+  // every element of qbar and kbar is written by the pooling kernel before
+  // it is read, so the array's previous contents need no clearing
+  return vsa_forward(plan, q, k, v, ws, sel, o, stream);
 }

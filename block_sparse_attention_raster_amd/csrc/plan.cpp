@@ -373,6 +373,7 @@ extern "C" const char* vsa_status_str(int s) {
     case VSA_ERR_OVERFLOW: return "offsets or counts overflow the kernels' index range";
     case VSA_ERR_DEVICE: return "current device is not gfx950 or a device query failed";
     case VSA_ERR_LAUNCH: return "kernel launch failed";
+    case VSA_ERR_SCRATCH: return "problem needs more scratch than the allocation-free entry point holds (32 MiB)";
     default: return "unknown status";
   }
 }

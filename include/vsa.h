@@ -77,7 +77,10 @@ enum {
                                 the kernels' index types                    */
   VSA_ERR_DEVICE = -6,       /* current device is not gfx950, or a HIP
                                 query failed                                */
-  VSA_ERR_LAUNCH = -7        /* a kernel launch reported an error           */
+  VSA_ERR_LAUNCH = -7,       /* a kernel launch reported an error           */
+  VSA_ERR_SCRATCH = -8       /* vsa_forward_noalloc: the problem needs more
+                                scratch (plan.workspace_bytes) than its
+                                fixed device array (32 MiB) holds           */
 };
 
 /* Element type of q, k, v and o. Softmax, row sums and the output
@@ -203,6 +206,23 @@ enum { VSA_SIDE_Q = 0, VSA_SIDE_K = 1 };
  * (user guide, "Wan top-k behavior": 120 cubes for the (31, 22, 40) grid
  * in (4, 8, 8) blocks, the edge cubes partial). */
 int vsa_block_counts(const vsa_plan_t* plan, int32_t side, int32_t* counts, int64_t len);
+
+/* vsa_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the pooled means kept
+ * in a fixed array of 32 MiB of device memory
+ * that the library holds on each device it runs on, from its first use
+ * there until the process ends, instead of a caller workspace. The caller
+ * still passes q, k, v, sel and o as for vsa_forward. Problems with
+ * plan->workspace_bytes above 32 MiB (32 heads of 960 cubes of 64 tokens
+ * need 31.5 MB; the Wan-shaped call 2.9 MB) return VSA_ERR_SCRATCH before any
+ * device work. The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Every call on one device shares that
+ * device's array: calls that overlap in time on one device (different
+ * streams, or host threads) race and give undefined results; calls in one
+ * stream order are safe. Asynchronous. */
+int vsa_forward_noalloc(const vsa_plan_t* plan, const void* q, const void* k,
+                        const void* v, int32_t* sel, void* o, void* stream);
 
 /* Formats the routing fields of the user guide's Wan log line
  * ("seq_len=..., dit_seq_shape=(T, H, W), block_size=(ct, ch, cw),
