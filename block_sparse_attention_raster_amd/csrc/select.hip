@@ -118,8 +118,13 @@ __device__ __forceinline__ void row_topk(const uint32_t* s, int nb, int topk, ui
 
 // row_topk with the row's keys held in registers: KPL keys per lane, key j
 // of the row at lane j % 64, slot j / 64 (nb <= 64*KPL). The histogram
-// passes then issue their LDS atomics back to back, with no reloads behind
-// them.
+// passes issue their LDS atomics back to back, with no reloads behind them.
+// After the first pass the bin that holds the topk-th key usually holds few
+// keys; when it holds at most 64 they are gathered into one register per
+// lane and the topk-th key is found among them directly (each candidate
+// counts the candidates at or above it: the wanted key is the largest one
+// with at least `remaining` of them), instead of by further passes. Both
+// ways find the same key, and the final pass is shared.
 template <int KPL>
 __device__ __forceinline__ void row_topk_regs(const uint32_t* s, int nb, int topk, uint32_t* wh, int lane,
                                               int32_t* out) {
@@ -143,9 +148,12 @@ __device__ __forceinline__ void row_topk_regs(const uint32_t* s, int nb, int top
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
   }
   const uint32_t range = mx - mn;
-  int hi = range ? 32 - __clz(range) : 0;
-  uint32_t prefix = 0;
-  int remaining = topk;
+  int hi = range ? 32 - __clz(range) : 0;  // offsets fit in `hi` bits
+  uint32_t prefix = 0;                      // known bits of the wanted offset above `hi`
+  int remaining = topk;                     // its rank among offsets matching the prefix
+  int bincnt = nb;                          // offsets matching the prefix
+  bool found_key = false;                   // the wanted key is known (thr_direct)
+  uint32_t thr_direct = 0;
   while (hi > 0) {
     const int lo = hi > 8 ? hi - 8 : 0;
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
@@ -169,26 +177,55 @@ __device__ __forceinline__ void row_topk_regs(const uint32_t* s, int nb, int top
     const int excl = incl - tot;
     const uint64_t hit = __ballot(excl < remaining && remaining <= incl);
     const int src = __ffsll((unsigned long long)hit) - 1;
-    int digit = 0, above = 0, cum = excl;
+    int digit = 0, above = 0, cnt = 0, cum = excl;
     bool found = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (!found && remaining <= cum + c[i]) {
         digit = 255 - 4 * lane - i;
         above = cum;
+        cnt = c[i];
         found = true;
       }
       cum += c[i];
     }
     digit = __shfl(digit, src, 64);
     above = __shfl(above, src, 64);
+    bincnt = __builtin_amdgcn_readfirstlane(__shfl(cnt, src, 64));
     prefix = (prefix << (hi - lo)) | (uint32_t)digit;
     remaining -= above;
     hi = lo;
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    if (hi > 0 && bincnt <= 64) {
+      // gather the bin's keys, one per lane (in no particular order)
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const bool in = lane + 64 * i < nb && ((kr[i] - mn) >> hi) == prefix;
+        const uint64_t m = __ballot(in);
+        if (in) wh[base + __popcll(m & ((1ull << lane) - 1ull))] = kr[i];
+        base += __popcll(m);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t mine = lane < bincnt ? wh[lane] : 0u;
+      int ge = 0;   // candidates at or above this lane's key
+      for (int t = 0; t < bincnt; ++t) ge += (uint32_t)__builtin_amdgcn_readlane((int)mine, t) >= mine;
+      uint32_t cand = lane < bincnt && ge >= remaining ? mine : 0u;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cand = max(cand, (uint32_t)__shfl_xor((int)cand, o, 64));
+      // keys above it: the bins above, and the candidates above it
+      const int gt_in_bin = __popcll(__ballot(lane < bincnt && mine > cand));
+      remaining -= gt_in_bin;   // equal keys still to take
+      thr_direct = cand;
+      found_key = true;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      break;
+    }
   }
-  const uint32_t thr = mn + prefix;
+  const uint32_t thr = found_key ? thr_direct : mn + prefix;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   int written = 0, eq_seen = 0;
 #pragma unroll
@@ -332,18 +369,30 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(Vs
     }
   }
   const float* kbase = kbar + (int64_t)bh * a.nb * D + 4 * g;
-  for (int cb = wave; cb * 16 < a.nb; cb += kMfmaWaves) {
+  // kbar rows of a block of 16 cubes, one lane group's head-dim slices
+  auto load_block = [&](int cb, f32x4 (&kx)[DQ / 4]) {
     const int col = cb * 16 + l16;
     const bool ok = col < a.nb;
     const f32x4* src = reinterpret_cast<const f32x4*>(kbase + (int64_t)(ok ? col : 0) * D);
+#pragma unroll
+    for (int i = 0; i < DQ / 4; ++i) kx[i] = ok ? src[4 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // the next block's rows are loaded while this block's MFMAs run
+  f32x4 kcur[DQ / 4], knext[DQ / 4];
+  if (wave * 16 < a.nb) load_block(wave, knext);
+  for (int cb = wave; cb * 16 < a.nb; cb += kMfmaWaves) {
+    const int col = cb * 16 + l16;
+    const bool ok = col < a.nb;
+#pragma unroll
+    for (int i = 0; i < DQ / 4; ++i) kcur[i] = knext[i];
+    if ((cb + kMfmaWaves) * 16 < a.nb) load_block(cb + kMfmaWaves, knext);
     float kv[DQ];
 #pragma unroll
     for (int i = 0; i < DQ / 4; ++i) {
-      const f32x4 x = ok ? src[4 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
-      kv[4 * i] = x[0];
-      kv[4 * i + 1] = x[1];
-      kv[4 * i + 2] = x[2];
-      kv[4 * i + 3] = x[3];
+      kv[4 * i] = kcur[i][0];
+      kv[4 * i + 1] = kcur[i][1];
+      kv[4 * i + 2] = kcur[i][2];
+      kv[4 * i + 3] = kcur[i][3];
     }
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
