@@ -590,6 +590,30 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     pn[pkb][phh] = __builtin_bit_cast(bf16x8, t);
   };
 
+  // soft_pair in three steps, for the pipelined step: the two exponentials,
+  // their packing into pn, and the pair's sum
+  auto soft_exp = [&](int kk, const f32x16 (&sa)[NKB], f32x2 (&ex)[NPAIR]) {
+    const int pkb = kk / 8, phh = (kk % 8) / 4, i = kk % 4, r = 8 * phh + 2 * i;
+    float e0 = __builtin_amdgcn_exp2f(xval(sa, pkb, r));
+    float e1 = __builtin_amdgcn_exp2f(xval(sa, pkb, r + 1));
+    pin(e0);
+    pin(e1);
+    ex[kk] = f32x2{e0, e1};
+  };
+  auto soft_pack = [&](int kk, const f32x2 (&ex)[NPAIR], uint32_t (&wp)[NPAIR], bf16x8 (&pn)[NKB][2]) {
+    const int pkb = kk / 8, phh = (kk % 8) / 4, i = kk % 4;
+    uint32_t w = E::pack2(ex[kk][0], ex[kk][1]);
+    pin(w);
+    wp[kk] = w;
+    u32x4 t = __builtin_bit_cast(u32x4, pn[pkb][phh]);
+    t[i] = w;
+    pn[pkb][phh] = __builtin_bit_cast(bf16x8, t);
+  };
+  auto soft_sum = [&](int kk, const uint32_t (&wp)[NPAIR], float (&ps)[4]) {
+    ps[kk % 4] = E::sum2(wp[kk], ps[kk % 4]);
+    pin(ps[kk % 4]);
+  };
+
   // The slow path of the softmax of one tile (the first tile, or a tile
   // whose sum of p left the bound in some row): rows that need it (both
   // lanes of a row decide together) raise m to their maximum x over the
@@ -649,6 +673,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     u32x2 vr[NDB][NVR];
     Pend pd;
     int tv[SPW];
+    f32x2 ex[NPAIR];       // exponentials of each pair, packed a slot later
+    uint32_t wp[NPAIR];    // packed pairs, summed a slot later
     // load j: slot-table read in slot rd_slot(j), addresses and copies in
     // slot NQ/2 + fire_gap(j) (odd slots when there is room, else one load
     // per slot)
@@ -695,10 +721,26 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
         oacc[db] = E::mfma(__builtin_bit_cast(bf16x8, w), pb[kb][hh], oacc[db]);
       }
       if constexpr (SOFT) {
+        // exponentials of this slot's pairs, packing of the previous slot's,
+        // sums of the slot before: no result is used in the slot that makes it
 #pragma unroll
-        for (int kk = p * (NPAIR / NP); kk < (p + 1) * (NPAIR / NP); ++kk) soft_pair(kk, sa, pn, ps);
+        for (int kk = p * (NPAIR / NP); kk < (p + 1) * (NPAIR / NP); ++kk) soft_exp(kk, sa, ex);
+        if (p >= 1) {
+#pragma unroll
+          for (int kk = (p - 1) * (NPAIR / NP); kk < p * (NPAIR / NP); ++kk) soft_pack(kk, ex, wp, pn);
+        }
+        if (p >= 2) {
+#pragma unroll
+          for (int kk = (p - 2) * (NPAIR / NP); kk < (p - 1) * (NPAIR / NP); ++kk) soft_sum(kk, wp, ps);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SOFT) {   // the last two slots' packing and sums
+#pragma unroll
+      for (int kk = (NP - 1) * (NPAIR / NP); kk < NPAIR; ++kk) soft_pack(kk, ex, wp, pn);
+#pragma unroll
+      for (int kk = (NP - 2) * (NPAIR / NP); kk < NPAIR; ++kk) soft_sum(kk, wp, ps);
     }
   };
 
