@@ -406,21 +406,22 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
   uint32_t kbase = 0; // its first row's byte offset
   int kn = 0;         // its valid tokens
   int ktab = 0;       // its slot-table base (extent type * V_k)
-  auto load_block = [&](int i) {
-    if (i < gk.Pb) {
-      const int s = i * gk.V;
-      kbase = (uint32_t)s * rowb;
-      kn = min(gk.V, gk.P - s);
-      ktab = 4 * gk.V;
-    } else {
-      const u32x2 e = blist[i - gk.Pb];
-      kbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)e[0]);
-      const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)e[1]);
-      kn = (int)(w & 0xFFFFu);
-      ktab = (int)(w >> 16);
-    }
+  u32x2 nxt;          // table entry of the block after it (an LDS read in flight)
+  auto fetch = [&](int i) { nxt = blist[min(max(i - gk.Pb, 0), a.topk - 1)]; };
+  // block i of the walk from nxt (a selected cube) or computed (a prefix
+  // block), without branches
+  auto next_block = [&](int i, uint32_t& base, int& n, int& tab) {
+    const uint32_t e0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)nxt[0]);
+    const uint32_t e1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)nxt[1]);
+    const bool pre = i < gk.Pb;
+    const int s = pre ? i * gk.V : 0;
+    base = pre ? (uint32_t)s * rowb : e0;
+    n = pre ? min(gk.V, gk.P - s) : (int)(e1 & 0xFFFFu);
+    tab = pre ? 4 * gk.V : (int)(e1 >> 16);
   };
-  load_block(0);
+  fetch(0);
+  next_block(0, kbase, kn, ktab);
+  fetch(1);
   // bound of every K load's row offset, and the V buffer resource: V of
   // this head, num_records = its byte span, so that offsets at or past it
   // (tail slots) read as zeros
@@ -446,23 +447,27 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     uint32_t ko[SPW];  // K byte offsets from kh
     uint32_t vo[SPW];  // V byte offsets from vh (out of range for tail slots)
   };
-  // describes the walker's current tile, then advances
+  // describes the walker's current tile, then advances (branch-free: the
+  // values are wave-uniform and selected, and the table entry of the block
+  // after the current one is read one call ahead)
   auto spec = [&](Spec& sp, uint64_t& m, bool& e) {
     const bool any = ibi < nkept;
+    const int nleft = any ? kn - kt0 : 0;
     sp.base = any ? kbase : 0u;
-    sp.nleft = any ? kn - kt0 : 0;
+    sp.nleft = nleft;
     sp.tk0 = ktab + kt0;
     e = any;
-    m = sp.nleft >= KT ? FULLM : ((1ull << sp.nleft) - 1ull);
-    if (any) {
-      if (sp.nleft > KT) {
-        kt0 += KT;
-      } else {
-        kt0 = 0;
-        ++ibi;
-        if (ibi < nkept) load_block(ibi);
-      }
-    }
+    m = nleft >= KT ? FULLM : ((1ull << nleft) - 1ull);
+    const bool adv = any && nleft <= KT;   // this tile ends its block
+    uint32_t nbase;
+    int nn, ntab;
+    next_block(ibi + 1, nbase, nn, ntab);
+    kbase = adv ? nbase : kbase;
+    kn = adv ? nn : kn;
+    ktab = adv ? ntab : ktab;
+    kt0 = adv ? 0 : (any ? kt0 + KT : kt0);
+    ibi = adv ? ibi + 1 : ibi;
+    fetch(ibi + 1);
   };
 
   // Thread (wave, lane) loads 16-byte unit s*64 + lane of each K and V tile
@@ -600,14 +605,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     pin(e1);
     ex[kk] = f32x2{e0, e1};
   };
+  // (pn[pkb][phh] is written whole once its four pairs are packed, so that
+  // its previous contents are dead while the step runs)
   auto soft_pack = [&](int kk, const f32x2 (&ex)[NPAIR], uint32_t (&wp)[NPAIR], bf16x8 (&pn)[NKB][2]) {
     const int pkb = kk / 8, phh = (kk % 8) / 4, i = kk % 4;
     uint32_t w = E::pack2(ex[kk][0], ex[kk][1]);
     pin(w);
     wp[kk] = w;
-    u32x4 t = __builtin_bit_cast(u32x4, pn[pkb][phh]);
-    t[i] = w;
-    pn[pkb][phh] = __builtin_bit_cast(bf16x8, t);
+    if (i == 3) pn[pkb][phh] = __builtin_bit_cast(bf16x8, u32x4{wp[kk - 3], wp[kk - 2], wp[kk - 1], w});
   };
   auto soft_sum = [&](int kk, const uint32_t (&wp)[NPAIR], float (&ps)[4]) {
     ps[kk % 4] = E::sum2(wp[kk], ps[kk % 4]);
