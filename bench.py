@@ -230,28 +230,49 @@ def _short_kernel(name: str) -> str:
     return m.group(1) if m else name[:60]
 
 
-def summarize_trace(path: str, skip: int) -> str:
-    """Per-kernel dispatch statistics of a rocprofv3 kernel-trace CSV,
-    dropping the first ``skip`` dispatches of each kernel (the warm-up
-    steps), in microseconds."""
+def cache_bandwidth() -> dict:
+    """Read bandwidth (GB/s) from windows that fit each XCD's L2 (2 MiB),
+    the MALL (16 to 128 MiB) or neither (2 GiB): the in-tree probe
+    block_sparse_attention_raster_amd/cache_probe (built with the library),
+    run as a child process."""
+    import subprocess
+    probe = os.path.join(ROOT, "block_sparse_attention_raster_amd", "cache_probe")
+    if not os.path.exists(probe):
+        raise RuntimeError("cache_probe is not built; run __graft_entry__.build() first")
+    r = subprocess.run([probe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError("cache_probe failed:\n" + r.stderr)
+    return json.loads(r.stdout)
+
+
+def summarize_trace(path: str, skip: int, take: int = 0) -> str:
+    """Per-kernel dispatch statistics of the library's kernels (vsa_*) in a
+    rocprofv3 kernel-trace CSV, dropping the first ``skip`` dispatches of
+    each kernel (the warm-up steps) and keeping the next ``take`` (all when
+    0), in microseconds. Other kernels (input copies, the cache flush) are
+    left out."""
     import csv
     rows = {}
     with open(path) as f:
         for r in csv.DictReader(f):
+            if "vsa_" not in r["Kernel_Name"]:
+                continue
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             rows.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), dur))
     lines = [f"{'kernel':<28}{'calls':>6}{'avg_us':>11}{'median_us':>11}{'min_us':>11}{'max_us':>11}"]
     total = {}
     for name, xs in rows.items():
         xs.sort()
-        d = np.array([x[1] for x in xs[skip:]]) if len(xs) > skip else np.array([])
+        kept = xs[skip:skip + take] if take > 0 else xs[skip:]
+        d = np.array([x[1] for x in kept])
         if d.size:
             total[name] = d
     grand = sum(d.sum() for d in total.values())
     for name, d in sorted(total.items(), key=lambda kv: -kv[1].sum()):
         lines.append(f"{_short_kernel(name):<28}{d.size:>6}{d.mean():>11.1f}{np.median(d):>11.1f}"
                      f"{d.min():>11.1f}{d.max():>11.1f}   {100.0 * d.sum() / grand:5.2f}%")
-    lines.append(f"(first {skip} dispatches of each kernel dropped)")
+    lines.append(f"(first {skip} dispatches of each kernel dropped"
+                 + (f", next {take} kept)" if take > 0 else ")"))
     return "\n".join(lines)
 
 
@@ -271,13 +292,21 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--cache-bandwidth", action="store_true",
+                    help="only measure read bandwidth from windows that fit the L2, the MALL or neither "
+                         "(the rooflines of the small-cube attention)")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="only print per-kernel statistics of a rocprofv3 kernel-trace CSV")
     ap.add_argument("--skip", type=int, default=0, help="with --summarize-trace: warm-up dispatches to drop")
+    ap.add_argument("--take", type=int, default=0,
+                    help="with --summarize-trace: dispatches to keep after the skipped ones (0: all)")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.skip))
+        print(summarize_trace(args.summarize_trace, args.skip, args.take))
+        return 0
+    if args.cache_bandwidth:
+        print(json.dumps(cache_bandwidth()), flush=True)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path shards over (batch, head) with no exchange "

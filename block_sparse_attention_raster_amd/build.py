@@ -1,4 +1,5 @@
-"""Builds libvsa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Builds libvsa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and the
+benchmark's read-bandwidth probe (cache_probe).
 
     python -m block_sparse_attention_raster_amd.build
 """
@@ -15,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvsa.so")
+PROBE = os.path.join(PKG, "cache_probe")   # read-bandwidth probe of the benchmark
 BUILD_DIR = os.path.join(PKG, "_build")
 
 HIP_SOURCES = ["api.hip", "pool.hip", "select.hip", "attend.hip"]
@@ -64,6 +66,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    _run([hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
+          "-packed-fp32-ops", os.path.join(CSRC, "cache_probe.hip"), "-o", PROBE + ".tmp"])
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
