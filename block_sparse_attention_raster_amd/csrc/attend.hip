@@ -24,8 +24,9 @@
 // LDS; query rows (read once) unravel k with multiply-high divisions. Query
 // blocks follow q's grid and cube shape, key blocks k's (the two differ when
 // q and k/v lie on different grids: fastbsa package page, section "Use").
-// The workgroup also describes its selected cubes once, in walk order, in an
-// LDS table, so moving from one kept block to the next costs one LDS read.
+// The workgroup also describes its kept blocks once, in walk order (the
+// prefix blocks, then the selected cubes), in an LDS table, so moving from
+// one kept block to the next costs one LDS read.
 //
 // Data movement. K and V tiles go from HBM straight into LDS with 16-byte
 // copies that bypass registers (global_load_lds for K; buffer_load ... lds
@@ -257,8 +258,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
   // [5][V_k] (+ padding) byte offsets from a key block's first row of its
   // compact slots: video cubes by extent type (0..3), prefix blocks (4)
   uint32_t* stab = reinterpret_cast<uint32_t*>(smem + 2 * NSTAGE * TILE_BYTES);
-  // [topk] selected cubes in walk order, as (first row's byte offset,
-  // n | slot-table base << 16)
+  // [Pb + topk] kept blocks in walk order (prefix blocks, then the selected
+  // cubes), as (first row's byte offset, n | slot-table base << 16)
   u32x2* blist = reinterpret_cast<u32x2*>(smem + 2 * NSTAGE * TILE_BYTES + slot_table_bytes(gk.V, KT));
   const uint32_t rowb = (uint32_t)a.ksn * 2u;   // bytes between key rows
 
@@ -322,15 +323,19 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
       }
       stab[idx] = t < 5 ? (uint32_t)row * rowb : 0u;
     }
-    // the selected cubes in walk order (ids clamped into range: other
-    // contents of sel stay in bounds)
+    // the prefix blocks, then the selected cubes in walk order (ids clamped
+    // into range: other contents of sel stay in bounds)
     const int32_t* selrow = sel + ((int64_t)(b * a.Hh + h) * a.nq + qblk) * a.topk;
-    for (int i = tid; i < a.topk; i += NW * 64) {
-      int t = i + rot;
-      if (t >= a.topk) t -= a.topk;
-      int c = selrow[t];
-      c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
-      const Blk d = describe_block(gk, gk.Pb + c);
+    for (int i = tid; i < gk.Pb + a.topk; i += NW * 64) {
+      int blk = i;
+      if (i >= gk.Pb) {
+        int t = i - gk.Pb + rot;
+        if (t >= a.topk) t -= a.topk;
+        int c = selrow[t];
+        c = c < 0 ? 0 : (c >= a.nb ? a.nb - 1 : c);
+        blk = gk.Pb + c;
+      }
+      const Blk d = describe_block(gk, blk);
       blist[i] = u32x2{(uint32_t)d.base * rowb, (uint32_t)d.n | ((uint32_t)(d.type * gk.V) << 16)};
     }
   }
@@ -398,8 +403,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
   float mneg = 0.f;               // -m (both lanes of a row agree)
   f32x16 negm = {};               // -m in every entry: with kPrescale the QK accumulators start there
 
-  // ---- kept-block walk (issue side): all prefix blocks of the key grid,
-  // then the selected cubes from the LDS table
+  // ---- kept-block walk (issue side) over the LDS table: all prefix blocks
+  // of the key grid, then the selected cubes
   const int nkept = gk.Pb + a.topk;
   int ibi = 0;        // current kept block
   int kt0 = 0;        // compact index of its next tile's first slot
@@ -407,20 +412,17 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
   int kn = 0;         // its valid tokens
   int ktab = 0;       // its slot-table base (extent type * V_k)
   u32x2 nxt;          // table entry of the block after it (an LDS read in flight)
-  auto fetch = [&](int i) { nxt = blist[min(max(i - gk.Pb, 0), a.topk - 1)]; };
-  // block i of the walk from nxt (a selected cube) or computed (a prefix
-  // block), without branches
-  auto next_block = [&](int i, uint32_t& base, int& n, int& tab) {
+  auto fetch = [&](int i) { nxt = blist[min(i, nkept - 1)]; };
+  // the block whose table entry nxt holds
+  auto next_block = [&](uint32_t& base, int& n, int& tab) {
     const uint32_t e0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)nxt[0]);
     const uint32_t e1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)nxt[1]);
-    const bool pre = i < gk.Pb;
-    const int s = pre ? i * gk.V : 0;
-    base = pre ? (uint32_t)s * rowb : e0;
-    n = pre ? min(gk.V, gk.P - s) : (int)(e1 & 0xFFFFu);
-    tab = pre ? 4 * gk.V : (int)(e1 >> 16);
+    base = e0;
+    n = (int)(e1 & 0xFFFFu);
+    tab = (int)(e1 >> 16);
   };
   fetch(0);
-  next_block(0, kbase, kn, ktab);
+  next_block(kbase, kn, ktab);
   fetch(1);
   // bound of every K load's row offset, and the V buffer resource: V of
   // this head, num_records = its byte span, so that offsets at or past it
@@ -461,7 +463,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     const bool adv = any && nleft <= KT;   // this tile ends its block
     uint32_t nbase;
     int nn, ntab;
-    next_block(ibi + 1, nbase, nn, ntab);
+    next_block(nbase, nn, ntab);
     kbase = adv ? nbase : kbase;
     kn = adv ? nn : kn;
     ktab = adv ? ntab : ktab;
@@ -605,8 +607,8 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     pin(e1);
     ex[kk] = f32x2{e0, e1};
   };
-  // (pn[pkb][phh] is written whole once its four pairs are packed, so that
-  // its previous contents are dead while the step runs)
+  // (pn[pkb][phh] is written whole once its four pairs are packed: the step
+  // packs into the P it reads, and a chunk's old P is dead by then)
   auto soft_pack = [&](int kk, const f32x2 (&ex)[NPAIR], uint32_t (&wp)[NPAIR], bf16x8 (&pn)[NKB][2]) {
     const int pkb = kk / 8, phh = (kk % 8) / 4, i = kk % 4;
     uint32_t w = E::pack2(ex[kk][0], ex[kk][1]);
@@ -655,31 +657,39 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
   // One pipelined step, in a fixed issue order of 32 (D = 128) or 16
   // (D = 64) slots of one MFMA each, fenced so that the compiler keeps the
   // order: first the QK MFMAs of tile `ks` with the K reads KA slots ahead
-  // and, in the last slots, the first head-dim block's V reads; then the
-  // P.V MFMAs of tile `vs_` (P of the previous step in pb) with the next
-  // block's V reads and, between them, the exponentials of the new scores
-  // in pairs packed into pn, with their sums. WITH_PV false (the first tile)
-  // runs only the QK half; SOFT false leaves the exponentials out. Tail
-  // tiles need no masking here: their key slots past the block's end repeat
-  // the block's first row and their V rows are zero; `tail_sum` then
-  // removes those slots from the row sum.
-  auto step = [&](auto with_pv, auto soft, int ks, int vs_, const bf16x8 (&pb)[NKB][2], bf16x8 (&pn)[NKB][2],
-                  f32x16 (&sa)[NKB], float (&ps)[4], const Spec& sp, int kstage, int vstage) {
+  // and, in the last slots, the V operands of the first P.V slots; then the
+  // P.V MFMAs of tile `vs_` (P of the previous step in pb) with their V
+  // operands read VRA slots ahead and, between them, the exponentials of
+  // the new scores in pairs, packed into pb as each 16-key chunk of the old
+  // P is done with, and their sums. `pre` runs in the first slot, after its
+  // MFMA (the walker's next tile: scalar work that the other wave's matrix
+  // ops cover). WITH_PV false (the first tile) runs only the QK half; SOFT
+  // false leaves the exponentials out. Tail tiles need no masking here:
+  // their key slots past the block's end repeat the block's first row and
+  // their V rows are zero; `tail_sum` then removes those slots from the row
+  // sum.
+  auto step = [&](auto with_pv, auto soft, auto pre, int ks, int vs_, bf16x8 (&pb)[NKB][2], f32x16 (&sa)[NKB],
+                  float (&ps)[4], const Spec& sp, int kstage, int vstage) {
     constexpr bool WITH_PV = decltype(with_pv)::value;
     constexpr bool SOFT = decltype(soft)::value;
-    constexpr int KA = 6;                   // K reads ahead of their MFMA
+    constexpr int KA = 4;                   // K reads ahead of their MFMA
     constexpr int NQ = NKB * NC;            // QK MFMAs
     constexpr int NDB = D / 32;             // head-dim blocks of P.V
-    constexpr int PPD = 2 * NKB;            // P.V MFMAs per head-dim block
-    constexpr int NP = NDB * PPD;           // P.V MFMAs
-    constexpr int RPS = NVR / PPD;          // V reads per P.V slot (next block)
-    static_assert(NVR % PPD == 0 && NPAIR % NP == 0, "schedule shape");
+    constexpr int NP = NDB * 2 * NKB;       // P.V MFMAs
+    constexpr int VRA = 4;                  // V operands read ahead of their MFMA
+    static_assert(NPAIR % NP == 0 && VRA <= NQ, "schedule shape");
     bf16x8 kop[NQ];
-    u32x2 vr[NDB][NVR];
+    u32x4 vop[NP];
     Pend pd;
     int tv[SPW];
     f32x2 ex[NPAIR];       // exponentials of each pair, packed a slot later
     uint32_t wp[NPAIR];    // packed pairs, summed a slot later
+    // V operand of P.V slot p: 16-key chunk p / NDB of head-dim block p % NDB
+    auto vop_read = [&](int p) {
+      const int ch = p / NDB, db = p % NDB;
+      const u32x2 a0 = vread(vs_, db, 2 * ch), a1 = vread(vs_, db, 2 * ch + 1);
+      vop[p] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    };
     // load j: slot-table read in slot rd_slot(j), addresses and copies in
     // slot NQ/2 + fire_gap(j) (odd slots when there is room, else one load
     // per slot)
@@ -692,14 +702,11 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
       if (qq + KA < NQ) kop[qq + KA] = kread(ks, (qq + KA) / NC, (qq + KA) % NC);
-      // first block's V reads, two per slot in the last NVR/2 slots
-      if (WITH_PV && qq >= NQ - NVR / 2) {
-        const int i = 2 * (qq - (NQ - NVR / 2));
-        vr[0][i] = vread(vs_, 0, i);
-        vr[0][i + 1] = vread(vs_, 0, i + 1);
-      }
+      // the first P.V slots' V operands in the last VRA slots
+      if (WITH_PV && qq >= NQ - VRA) vop_read(qq - (NQ - VRA));
       const int kb = qq / NC, c = qq % NC;
       sa[kb] = E::mfma(kop[qq], qreg[c], c != 0 ? sa[kb] : E::kPrescale ? negm : f32x16{});
+      if (qq == 0) pre();
       // the refill of the stage freed by this step's barrier: slot-table
       // read of load j in slot 1 + 2j, its addresses and copies in slot
       // NQ/2 + 2j
@@ -713,17 +720,15 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // P.V with the head-dim block innermost: chunk ch of P is last read in
+    // slot NDB*ch + NDB - 1, and the new P of that chunk is packed into the
+    // same registers from slot NDB*(ch + 1) on.
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int db = p / PPD, kb = (p % PPD) / 2, hh = p % 2;
+      const int ch = p / NDB, db = p % NDB;
       if constexpr (WITH_PV) {
-        if (db + 1 < NDB) {
-#pragma unroll
-          for (int e = 0; e < RPS; ++e) vr[db + 1][RPS * (p % PPD) + e] = vread(vs_, db + 1, RPS * (p % PPD) + e);
-        }
-        const u32x4 w = {vr[db][4 * kb + 2 * hh][0], vr[db][4 * kb + 2 * hh][1], vr[db][4 * kb + 2 * hh + 1][0],
-                         vr[db][4 * kb + 2 * hh + 1][1]};
-        oacc[db] = E::mfma(__builtin_bit_cast(bf16x8, w), pb[kb][hh], oacc[db]);
+        if (p + VRA < NP) vop_read(p + VRA);
+        oacc[db] = E::mfma(__builtin_bit_cast(bf16x8, vop[p]), pb[ch / 2][ch % 2], oacc[db]);
       }
       if constexpr (SOFT) {
         // exponentials of this slot's pairs, packing of the previous slot's,
@@ -732,7 +737,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
         for (int kk = p * (NPAIR / NP); kk < (p + 1) * (NPAIR / NP); ++kk) soft_exp(kk, sa, ex);
         if (p >= 1) {
 #pragma unroll
-          for (int kk = (p - 1) * (NPAIR / NP); kk < p * (NPAIR / NP); ++kk) soft_pack(kk, ex, wp, pn);
+          for (int kk = (p - 1) * (NPAIR / NP); kk < p * (NPAIR / NP); ++kk) soft_pack(kk, ex, wp, pb);
         }
         if (p >= 2) {
 #pragma unroll
@@ -743,7 +748,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     }
     if constexpr (SOFT) {   // the last two slots' packing and sums
 #pragma unroll
-      for (int kk = (NP - 1) * (NPAIR / NP); kk < NPAIR; ++kk) soft_pack(kk, ex, wp, pn);
+      for (int kk = (NP - 1) * (NPAIR / NP); kk < NPAIR; ++kk) soft_pack(kk, ex, wp, pb);
 #pragma unroll
       for (int kk = (NP - 2) * (NPAIR / NP); kk < NPAIR; ++kk) soft_sum(kk, wp, ps);
     }
@@ -855,7 +860,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
     if constexpr (ACTIVE) {
       f32x16 sa[NKB];
       float ps[4];
-      step(F_{}, F_{}, 0, 0, pb, pb, sa, ps, sp, AHEAD, AHEAD - 1);
+      step(F_{}, F_{}, [] {}, 0, 0, pb, sa, ps, sp, AHEAD, AHEAD - 1);
       lrow = raise_offset(sa, pb, true, true);
       if (mring[0] != FULLM) tail_sum(mring[0], last_p(pb));
     } else {
@@ -869,7 +874,7 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
       const bool have = ering[0];
       const int fst = cur + AHEAD >= NSTAGE ? cur + AHEAD - NSTAGE : cur + AHEAD;   // K refill
       const int vfst = fst == 0 ? NSTAGE - 1 : fst - 1;                               // V refill
-      if (have) spec(sp, mring[AHEAD], ering[AHEAD]);
+      if (!ACTIVE && have) spec(sp, mring[AHEAD], ering[AHEAD]);
       // the last P.V reads V of the last tile, copied one step after its K
       if constexpr (BSTEP == 1) {
         if (have) wait_first(); else wait_vmcnt<0>();
@@ -883,20 +888,14 @@ void vsa_attend_kernel(VsaArgs a, const __bf16* __restrict__ q, const __bf16* __
         break;
       }
       if constexpr (ACTIVE) {
-        bf16x8 pn[NKB][2];
         f32x16 sa[NKB];
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
-        step(T_{}, T_{}, cur, prev, pb, pn, sa, ps, sp, fst, vfst);
+        step(T_{}, T_{}, [&] { spec(sp, mring[AHEAD], ering[AHEAD]); }, cur, prev, pb, sa, ps, sp, fst, vfst);
         const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         const bool need = !(psum <= E::kSumLimit);   // NaN or inf included
-        if (__ballot(need) != 0) lrow += raise_offset(sa, pn, need, false);
+        if (__ballot(need) != 0) lrow += raise_offset(sa, pb, need, false);
         else lrow += psum;
-        if (mring[0] != FULLM) tail_sum(mring[0], last_p(pn));
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          pb[kb][0] = pn[kb][0];
-          pb[kb][1] = pn[kb][1];
-        }
+        if (mring[0] != FULLM) tail_sum(mring[0], last_p(pb));
       } else {
         fire_all(fst, vfst);
       }
@@ -955,7 +954,7 @@ int resident_per_xcd(const void* func, int threads, size_t lds) {
 // kept-block table.
 template <int D, int NSTAGE, int KT>
 size_t attend_lds_bytes(const VsaArgs& a) {
-  return (size_t)2 * NSTAGE * KT * D * 2 + slot_table_bytes(a.gk.V, KT) + (size_t)a.topk * 8;
+  return (size_t)2 * NSTAGE * KT * D * 2 + slot_table_bytes(a.gk.V, KT) + (size_t)(a.gk.Pb + a.topk) * 8;
 }
 
 template <int D, int NW, int NSTAGE, int KT, int WPE, bool F16, int BSTEP>
