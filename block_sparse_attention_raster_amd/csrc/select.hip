@@ -6,7 +6,9 @@
 // them against every cube, s[i][j] = qbar_i . kbar_j in float32 (the positive
 // factor head_dim^-1/2 does not change the order and is left out). Each score
 // is stored as an order-preserving 32-bit key in LDS; then one wave per row
-// finds the topk-th largest key exactly by radix selection. Keys above it are
+// finds the topk-th largest key exactly (a histogram over the row's score
+// range, then the few keys of the bin that holds it ranked directly, with
+// radix selection over the key bits as the general fallback). Keys above it are
 // kept; among keys equal to it the lowest cube ids are kept ("FastVideo VSA"
 // user guide, section "Wan top-k behavior": top-k is the number of
 // key/value blocks kept per query block). The kept ids are written in
@@ -25,12 +27,44 @@ constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kColChunk = 64;   // cubes scored per LDS stage
 
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+// Cross-lane steps on the vector ALU (DPP row operations and the permlane
+// swaps), with no LDS round trip.
+template <int CTRL, int ROW_MASK = 0xF, bool ZERO_FILL = true>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, ZERO_FILL);
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// x op'd over all 64 lanes, in every lane
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_all(uint32_t x, Op op) {
+  x = op(x, (uint32_t)dpp<kQuadXor1>((int)x));
+  x = op(x, (uint32_t)dpp<kQuadXor2>((int)x));
+  x = op(x, (uint32_t)dpp<kRowHalfMirror>((int)x));
+  x = op(x, (uint32_t)dpp<kRowMirror>((int)x));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(r32[0], r32[1]);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  return wave_all(x, [](uint32_t u, uint32_t v) { return u < v ? u : v; });
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  return wave_all(x, [](uint32_t u, uint32_t v) { return u > v ? u : v; });
+}
+
+// inclusive prefix sum over the 64 lanes: within each row of 16 lanes by
+// shifts of 1, 2, 4 and 8, then the row totals carried across rows
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += dpp<kRowShr1>(x);
+  x += dpp<kRowShr2>(x);
+  x += dpp<kRowShr4>(x);
+  x += dpp<kRowShr8>(x);
+  x += dpp<kRowBcast15, 0xA>(x);
+  x += dpp<kRowBcast31, 0xC>(x);
   return x;
 }
 
@@ -47,11 +81,8 @@ __device__ __forceinline__ void row_topk(const uint32_t* s, int nb, int topk, ui
     mn = min(mn, key);
     mx = max(mx, key);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   const uint32_t range = mx - mn;
   int hi = range ? 32 - __clz(range) : 0;  // offsets fit in `hi` bits
   uint32_t prefix = 0;                      // known bits of the wanted offset above `hi`
@@ -74,7 +105,7 @@ __device__ __forceinline__ void row_topk(const uint32_t* s, int nb, int topk, ui
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = (int)wh[255 - 4 * lane - i];
     const int tot = c[0] + c[1] + c[2] + c[3];
-    const int incl = wave_inclusive_scan(tot, lane);
+    const int incl = wave_inclusive_scan(tot);
     const int excl = incl - tot;
     const uint64_t hit = __ballot(excl < remaining && remaining <= incl);
     const int src = __ffsll((unsigned long long)hit) - 1;
@@ -89,8 +120,8 @@ __device__ __forceinline__ void row_topk(const uint32_t* s, int nb, int topk, ui
       }
       cum += c[i];
     }
-    digit = __shfl(digit, src, 64);
-    above = __shfl(above, src, 64);
+    digit = __builtin_amdgcn_readlane(digit, src);
+    above = __builtin_amdgcn_readlane(above, src);
     prefix = (prefix << (hi - lo)) | (uint32_t)digit;
     remaining -= above;
     hi = lo;
@@ -125,6 +156,41 @@ __device__ __forceinline__ void row_topk(const uint32_t* s, int nb, int topk, ui
 // counts the candidates at or above it: the wanted key is the largest one
 // with at least `remaining` of them), instead of by further passes. Both
 // ways find the same key, and the final pass is shared.
+// The float whose order-preserving key is k.
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Among the candidate keys `mine` (lanes < cnt, in no particular order),
+// the largest key with at least `remaining` candidates at or above it.
+// Returns it and lowers `remaining` by the candidates above it (leaving the
+// number of keys equal to it still to take); `neq` is set to the whole
+// number of keys equal to it.
+__device__ __forceinline__ uint32_t rank_candidates(uint32_t mine, int cnt, int lane, int& remaining, int& neq) {
+  int ge = 0;   // candidates at or above this lane's key
+  for (int t = 0; t < cnt; ++t) ge += (uint32_t)__builtin_amdgcn_readlane((int)mine, t) >= mine;
+  uint32_t cand = lane < cnt && ge >= remaining ? mine : 0u;
+  cand = wave_max(cand);
+  remaining -= __popcll(__ballot(lane < cnt && mine > cand));
+  neq = __popcll(__ballot(lane < cnt && mine == cand));
+  return cand;
+}
+
+// row_topk with the row's keys held in registers: KPL keys per lane, key j
+// of the row at lane j % 64, slot j / 64 (nb <= 64*KPL). The first
+// histogram spreads over the row's score range linearly: bin
+// floor((x - min) * 256 / (max - min)) of the score x is monotone in x, so
+// the bins above the one that holds the topk-th key hold exactly the keys
+// greater than every key in it. That bin usually holds a few keys; when it
+// holds at most 64 they are gathered into one register per lane and the
+// topk-th key is found among them directly (each candidate counts the
+// candidates at or above it: the wanted key is the largest one with at
+// least `remaining` of them). Otherwise (many equal or clustered scores,
+// or a range that is not finite) the keys are searched by radix selection
+// over their bits, 8 at a time, from the highest bit in which the keys'
+// offsets from the row minimum differ; its passes issue their LDS atomics
+// back to back, and the same early exit applies after each pass. All ways
+// find the same key, and the final pass is shared.
 template <int KPL>
 __device__ __forceinline__ void row_topk_regs(const uint32_t* s, int nb, int topk, uint32_t* wh, int lane,
                                               int32_t* out) {
@@ -142,92 +208,137 @@ __device__ __forceinline__ void row_topk_regs(const uint32_t* s, int nb, int top
       mx = max(mx, kr[i]);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   const uint32_t range = mx - mn;
-  int hi = range ? 32 - __clz(range) : 0;  // offsets fit in `hi` bits
-  uint32_t prefix = 0;                      // known bits of the wanted offset above `hi`
-  int remaining = topk;                     // its rank among offsets matching the prefix
-  int bincnt = nb;                          // offsets matching the prefix
-  bool found_key = false;                   // the wanted key is known (thr_direct)
+  int remaining = topk;      // rank of the wanted key among the keys still in play
+  bool found_key = false;    // the wanted key is known (thr_direct)
   uint32_t thr_direct = 0;
-  while (hi > 0) {
-    const int lo = hi > 8 ? hi - 8 : 0;
-    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+  int neq = -1;              // keys equal to the wanted key, when known
+
+  // the bin counts of this wave's histogram, read as four bins per lane from
+  // the top, and the bin that holds the remaining-th key from the top: its
+  // index, the keys above it and the keys in it
+  auto find_bin = [&](int& digit, int& above, int& cnt) {
+    int c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = (int)wh[255 - 4 * lane - i];
+    const int tot = c[0] + c[1] + c[2] + c[3];
+    const int incl = wave_inclusive_scan(tot);
+    const int excl = incl - tot;
+    const uint64_t hit = __ballot(excl < remaining && remaining <= incl);
+    const int src = __ffsll((unsigned long long)hit) - 1;
+    int d = 0, ab = 0, cn = 0, cum = excl;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!found && remaining <= cum + c[i]) {
+        d = 255 - 4 * lane - i;
+        ab = cum;
+        cn = c[i];
+        found = true;
+      }
+      cum += c[i];
+    }
+    digit = __builtin_amdgcn_readlane(d, src);
+    above = __builtin_amdgcn_readlane(ab, src);
+    cnt = __builtin_amdgcn_readlane(cn, src);
+  };
+  auto clear_hist = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) wh[lane * 4 + i] = 0;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+  };
+  auto hist_done = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  };
+  // gather the keys for which `in(i)` holds (at most 64), one per lane, and
+  // rank them
+  auto gather_rank = [&](auto in, int cnt) {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const bool take = lane + 64 * i < nb && in(i);
+      const uint64_t m = __ballot(take);
+      if (take) wh[base + __popcll(m & ((1ull << lane) - 1ull))] = kr[i];
+      base += __popcll(m);
+    }
+    hist_done();
+    const uint32_t mine = lane < cnt ? wh[lane] : 0u;
+    thr_direct = rank_candidates(mine, cnt, lane, remaining, neq);
+    found_key = true;
+    hist_done();
+  };
+
+  // linear first pass over the score values
+  const float fmn = key_value(mn), fmx = key_value(mx);
+  const float scale = 256.f / (fmx - fmn);
+  if (range != 0u && __builtin_isfinite(fmn) && __builtin_isfinite(fmx) && __builtin_isfinite(scale) && scale > 0.f) {
+    int bin[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      bin[i] = lane + 64 * i < nb ? min(255, (int)((key_value(kr[i]) - fmn) * scale)) : 0;
+    clear_hist();
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (lane + 64 * i < nb) atomicAdd(&wh[bin[i]], 1u);
+    hist_done();
+    int digit, above, cnt;
+    find_bin(digit, above, cnt);
+    hist_done();
+    if (cnt <= 64) {
+      remaining -= above;
+      gather_rank([&](int i) { return bin[i] == digit; }, cnt);
+    }
+  }
+
+  // radix selection over the key bits
+  int hi = (found_key || range == 0u) ? 0 : 32 - __clz(range);   // offsets fit in `hi` bits
+  uint32_t prefix = 0;   // known bits of the wanted offset above `hi`
+  while (hi > 0) {
+    const int lo = hi > 8 ? hi - 8 : 0;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    clear_hist();
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const uint32_t off = kr[i] - mn;
       const uint32_t top = hi >= 32 ? 0u : (off >> hi);
       if (lane + 64 * i < nb && top == prefix) atomicAdd(&wh[(off >> lo) & dmask], 1u);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    int c[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = (int)wh[255 - 4 * lane - i];
-    const int tot = c[0] + c[1] + c[2] + c[3];
-    const int incl = wave_inclusive_scan(tot, lane);
-    const int excl = incl - tot;
-    const uint64_t hit = __ballot(excl < remaining && remaining <= incl);
-    const int src = __ffsll((unsigned long long)hit) - 1;
-    int digit = 0, above = 0, cnt = 0, cum = excl;
-    bool found = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!found && remaining <= cum + c[i]) {
-        digit = 255 - 4 * lane - i;
-        above = cum;
-        cnt = c[i];
-        found = true;
-      }
-      cum += c[i];
-    }
-    digit = __shfl(digit, src, 64);
-    above = __shfl(above, src, 64);
-    bincnt = __builtin_amdgcn_readfirstlane(__shfl(cnt, src, 64));
+    hist_done();
+    int digit, above, cnt;
+    find_bin(digit, above, cnt);
     prefix = (prefix << (hi - lo)) | (uint32_t)digit;
     remaining -= above;
     hi = lo;
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (hi > 0 && bincnt <= 64) {
-      // gather the bin's keys, one per lane (in no particular order)
-      int base = 0;
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const bool in = lane + 64 * i < nb && ((kr[i] - mn) >> hi) == prefix;
-        const uint64_t m = __ballot(in);
-        if (in) wh[base + __popcll(m & ((1ull << lane) - 1ull))] = kr[i];
-        base += __popcll(m);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      const uint32_t mine = lane < bincnt ? wh[lane] : 0u;
-      int ge = 0;   // candidates at or above this lane's key
-      for (int t = 0; t < bincnt; ++t) ge += (uint32_t)__builtin_amdgcn_readlane((int)mine, t) >= mine;
-      uint32_t cand = lane < bincnt && ge >= remaining ? mine : 0u;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) cand = max(cand, (uint32_t)__shfl_xor((int)cand, o, 64));
-      // keys above it: the bins above, and the candidates above it
-      const int gt_in_bin = __popcll(__ballot(lane < bincnt && mine > cand));
-      remaining -= gt_in_bin;   // equal keys still to take
-      thr_direct = cand;
-      found_key = true;
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
+    hist_done();
+    if (hi == 0) neq = cnt;   // the last digit's bin holds exactly the keys equal to it
+    if (hi > 0 && cnt <= 64) {
+      gather_rank([&](int i) { return ((kr[i] - mn) >> hi) == prefix; }, cnt);
       break;
     }
   }
+  if (range == 0u) neq = nb;   // every key equals the row minimum
   const uint32_t thr = found_key ? thr_direct : mn + prefix;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  int written = 0, eq_seen = 0;
+  int written = 0;
+  if (neq == remaining) {
+    // every key equal to the threshold is taken: the kept keys are those at
+    // or above it
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int j = lane + 64 * i;
+      const bool take = j < nb && kr[i] >= thr;
+      const uint64_t tm = __ballot(take);
+      const int pos = written + __popcll(tm & lt_mask);
+      if (take && pos < topk) out[pos] = j;
+      written += __popcll(tm);
+    }
+    return;
+  }
+  int eq_seen = 0;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int j = lane + 64 * i;
@@ -370,39 +481,44 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(Vs
   }
   const float* kbase = kbar + (int64_t)bh * a.nb * D + 4 * g;
   // kbar rows of a block of 16 cubes, one lane group's head-dim slices
+  // (columns past the last cube read its row: their scores are not stored)
+  const int nblk = (a.nb + 15) / 16;
   auto load_block = [&](int cb, f32x4 (&kx)[DQ / 4]) {
-    const int col = cb * 16 + l16;
-    const bool ok = col < a.nb;
-    const f32x4* src = reinterpret_cast<const f32x4*>(kbase + (int64_t)(ok ? col : 0) * D);
+    const int col = min(cb * 16 + l16, a.nb - 1);
+    const f32x4* src = reinterpret_cast<const f32x4*>(kbase + (int64_t)col * D);
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) kx[i] = ok ? src[4 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < DQ / 4; ++i) kx[i] = src[4 * i];
+    __builtin_amdgcn_sched_barrier(0);   // issued before the MFMAs that follow
   };
-  // the next block's rows are loaded while this block's MFMAs run
-  f32x4 kcur[DQ / 4], knext[DQ / 4];
-  if (wave * 16 < a.nb) load_block(wave, knext);
-  for (int cb = wave; cb * 16 < a.nb; cb += kMfmaWaves) {
-    const int col = cb * 16 + l16;
-    const bool ok = col < a.nb;
-#pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) kcur[i] = knext[i];
-    if ((cb + kMfmaWaves) * 16 < a.nb) load_block(cb + kMfmaWaves, knext);
-    float kv[DQ];
-#pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) {
-      kv[4 * i] = kcur[i][0];
-      kv[4 * i + 1] = kcur[i][1];
-      kv[4 * i + 2] = kcur[i][2];
-      kv[4 * i + 3] = kcur[i][3];
-    }
+  auto score_block = [&](int cb, const f32x4 (&kx)[DQ / 4]) {
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < DQ; c += 2) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[c], kv[c], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[c + 1], kv[c + 1], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[c], kx[c / 4][c % 4], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[c + 1], kx[c / 4][(c + 1) % 4], acc1, 0, 0, 0);
     }
-    if (ok) {
+    const int col = cb * 16 + l16;
+    if (col < a.nb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[(4 * g + r) * a.nb + col] = orderable_key(acc0[r] + acc1[r]);
+    }
+  };
+  // two register buffers: the next block of this wave (every eighth) is
+  // loaded while this one's MFMAs run; the load after the last block
+  // repeats it, so that every iteration issues the same loads
+  f32x4 kb0[DQ / 4], kb1[DQ / 4];
+  const int last = nblk - 1;
+  if (wave < nblk) {
+    load_block(wave, kb0);
+    for (int cb = wave;;) {
+      load_block(min(cb + kMfmaWaves, last), kb1);
+      score_block(cb, kb0);
+      cb += kMfmaWaves;
+      if (cb >= nblk) break;
+      load_block(min(cb + kMfmaWaves, last), kb0);
+      score_block(cb, kb1);
+      cb += kMfmaWaves;
+      if (cb >= nblk) break;
     }
   }
   __syncthreads();
