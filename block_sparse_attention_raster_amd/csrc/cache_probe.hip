@@ -1,7 +1,7 @@
 // Read bandwidth of the memory hierarchy, for the rooflines of the kernels
 // that live on cache reuse (attention over small cubes): every workgroup
-// reads 4 MiB with 16-byte loads from a window of S bytes, wrapping, from a
-// workgroup-dependent start; S = 2 MiB stays in each XCD's L2, 16 to
+// reads 4 MiB with 16-byte loads, eight in flight per thread, from a window
+// of S bytes, wrapping, from a workgroup-dependent start; S = 2 MiB stays in each XCD's L2, 16 to
 // 128 MiB stay in the memory-side cache (MALL), 2 GiB streams from HBM.
 // Prints one JSON object (GB/s, median of three timed runs after one warm
 // run). Built next to the library; run by the benchmark's --cache-bandwidth.
@@ -16,17 +16,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-__global__ __launch_bounds__(256) void read_window(const f32x4* __restrict__ buf, size_t nvec, size_t per_block,
+// Every thread keeps kInFlight independent 16-byte loads in flight (a single
+// load per thread would measure the latency of the level, not its
+// bandwidth). Windows are powers of two, so the wrap is a mask.
+constexpr int kInFlight = 8;
+
+__global__ __launch_bounds__(256) void read_window(const f32x4* __restrict__ buf, size_t mask, size_t per_block,
                                                    float* __restrict__ out) {
-  size_t start = ((size_t)blockIdx.x * 4099u * 256u) % nvec;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (size_t i = threadIdx.x; i < per_block; i += 256) {
-    size_t idx = start + i;
-    if (idx >= nvec) idx -= nvec;
-    if (idx >= nvec) idx %= nvec;
-    acc += buf[idx];
+  const size_t start = ((size_t)blockIdx.x * 4099u * 256u) & mask;
+  f32x4 acc[kInFlight];
+#pragma unroll
+  for (int k = 0; k < kInFlight; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (size_t i = threadIdx.x; i < per_block; i += 256 * kInFlight) {
+    f32x4 v[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) v[k] = buf[(start + i + (size_t)k * 256) & mask];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) acc[k] += v[k];
   }
-  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
+  f32x4 t = acc[0];
+#pragma unroll
+  for (int k = 1; k < kInFlight; ++k) t += acc[k];
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = t[0] + t[1] + t[2] + t[3];
 }
 
 bool ok(hipError_t e, const char* what) {
@@ -54,11 +65,11 @@ int main() {
   std::printf("{\"read_gbs\": {");
   bool first = true;
   for (size_t w : wins) {
-    const size_t nvec = w / 16;
+    const size_t mask = w / 16 - 1;   // windows are powers of two
     std::vector<float> ms;
     for (int rep = 0; rep < 4; ++rep) {
       if (!ok(hipEventRecord(e0), "record")) return 1;
-      hipLaunchKernelGGL(read_window, dim3(blocks), dim3(256), 0, 0, buf, nvec, per_block, out);
+      hipLaunchKernelGGL(read_window, dim3(blocks), dim3(256), 0, 0, buf, mask, per_block, out);
       if (!ok(hipGetLastError(), "launch") || !ok(hipEventRecord(e1), "record") ||
           !ok(hipEventSynchronize(e1), "sync"))
         return 1;
