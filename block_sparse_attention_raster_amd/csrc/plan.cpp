@@ -182,7 +182,7 @@ extern "C" int vsa_plan(const vsa_problem* pr, vsa_plan_t* out) {
   // (4 bytes per cube and row); keep it within the budget and prefer enough
   // workgroups to cover the machine.
   // Up to VSA_SELECT_MFMA_MAX_BLOCKS cubes the matrix-core kernel takes 16
-  // rows per workgroup.
+  // or 32 rows per workgroup (its launcher decides by LDS and grid size).
   int rows = VSA_SELECT_MAX_ROWS;
   if (nb > VSA_SELECT_MFMA_MAX_BLOCKS) {
     while (rows > 1 && (int64_t)rows * nb * 4 > VSA_SELECT_SCORE_LDS) rows /= 2;

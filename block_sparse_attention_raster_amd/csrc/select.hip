@@ -433,26 +433,28 @@ __global__ __launch_bounds__(kSelThreads) void vsa_score_topk_kernel(VsaArgs a, 
 }
 
 // Scores on the fp32 matrix cores (v_mfma_f32_16x16x4f32) for up to
-// VSA_SELECT_MFMA_MAX_BLOCKS cubes: one workgroup takes 16 query blocks of one head; each
-// wave takes every eighth block of 16 cubes. In one MFMA step, lane group
-// g = lane/16 contributes head-dim index 16*(c/4) + 4*g + c%4, so one
-// 16-byte load instruction reads 64 contiguous bytes of each of 16 qbar or
-// kbar rows, straight from global memory (L2-resident: workgroups of one
-// head run on one XCD). The 16x16 result lands as keys in LDS;
-// then each of the eight waves runs row_topk on two rows.
-constexpr int kMfmaRows = 16;
-constexpr int kMfmaWaves = 8;  // two rows per wave in the top-k phase
-
-template <int D, int KPL>
-__global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(VsaArgs a, const float* __restrict__ qbar,
+// VSA_SELECT_MFMA_MAX_BLOCKS cubes: one workgroup of 8*RG waves takes 16*RG
+// query blocks of one head, with their qbar rows in LDS; each wave takes
+// every (8*RG)-th block of 16 cubes, loads its kbar rows straight from
+// global memory (L2-resident: workgroups of one head run on one XCD) while
+// the previous block's MFMAs run, and scores it against all RG groups of 16
+// rows. In one MFMA step, lane group g = lane/16 contributes head-dim index
+// 16*(c/4) + 4*g + c%4, so one 16-byte load reads 64 contiguous bytes of each
+// of 16 kbar rows. Every workgroup streams the head's whole kbar through its
+// CU, so two row groups halve that traffic; they need 32 score rows of LDS,
+// which fit up to about a thousand cubes. The 16x16 results land as keys in
+// LDS; then each wave runs row_topk on two rows.
+template <int D, int KPL, int RG>
+__global__ __launch_bounds__(RG * 8 * 64) void vsa_score_topk_mfma_kernel(VsaArgs a, const float* __restrict__ qbar,
                                                                           const float* __restrict__ kbar,
                                                                           int32_t* __restrict__ sel) {
+  constexpr int kRows = 16 * RG, kWaves = 8 * RG;
   constexpr int DQ = D / 4;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint32_t* sc = reinterpret_cast<uint32_t*>(smem);   // [16][nb]
-  uint32_t* hist = sc + kMfmaRows * a.nb;               // [waves][256]
+  uint32_t* sc = reinterpret_cast<uint32_t*>(smem);   // [rows][nb]
+  uint32_t* hist = sc + kRows * a.nb;                   // [waves][256]
 
-  const int groups = (a.nq + kMfmaRows - 1) / kMfmaRows;
+  const int groups = (a.nq + kRows - 1) / kRows;
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
   // id is remapped to give each XCD a contiguous range (whole heads): a
   // head's kbar then stays in one XCD's L2
@@ -461,27 +463,20 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(Vs
   const int lid = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (lid >= nwg) return;
   const int bh = lid / groups;
-  const int row0 = (lid - bh * groups) * kMfmaRows;
-  const int nrows = min(kMfmaRows, a.nq - row0);
+  const int row0 = (lid - bh * groups) * kRows;
+  const int nrows = min(kRows, a.nq - row0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
 
-  float qv[DQ];
-  {
-    const bool ok = l16 < nrows;
-    const f32x4* src = reinterpret_cast<const f32x4*>(qbar + ((int64_t)bh * a.nq + row0 + (ok ? l16 : 0)) * D + 4 * g);
-#pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) {
-      const f32x4 x = ok ? src[4 * i] : f32x4{0.f, 0.f, 0.f, 0.f};
-      qv[4 * i] = x[0];
-      qv[4 * i + 1] = x[1];
-      qv[4 * i + 2] = x[2];
-      qv[4 * i + 3] = x[3];
-    }
+  // the group's qbar rows in LDS, read per MFMA step
+  f32x4* qs = reinterpret_cast<f32x4*>(hist + kWaves * 256);   // [rows][DQ]
+  for (int i = tid; i < kRows * DQ; i += kWaves * 64) {
+    const int r = i / DQ;
+    qs[i] = r < nrows ? reinterpret_cast<const f32x4*>(qbar + ((int64_t)bh * a.nq + row0 + r) * D)[i - r * DQ]
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __syncthreads();
   const float* kbase = kbar + (int64_t)bh * a.nb * D + 4 * g;
-  // kbar rows of a block of 16 cubes, one lane group's head-dim slices
-  // (columns past the last cube read its row: their scores are not stored)
   const int nblk = (a.nb + 15) / 16;
   auto load_block = [&](int cb, f32x4 (&kx)[DQ / 4]) {
     const int col = min(cb * 16 + l16, a.nb - 1);
@@ -490,47 +485,69 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void vsa_score_topk_mfma_kernel(Vs
     for (int i = 0; i < DQ / 4; ++i) kx[i] = src[4 * i];
     __builtin_amdgcn_sched_barrier(0);   // issued before the MFMAs that follow
   };
+  // one kbar block against every row group of the workgroup
   auto score_block = [&](int cb, const f32x4 (&kx)[DQ / 4]) {
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < DQ; c += 2) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[c], kx[c / 4][c % 4], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[c + 1], kx[c / 4][(c + 1) % 4], acc1, 0, 0, 0);
-    }
     const int col = cb * 16 + l16;
-    if (col < a.nb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[(4 * g + r) * a.nb + col] = orderable_key(acc0[r] + acc1[r]);
+    for (int rg = 0; rg < RG; ++rg) {
+      const f32x4* qrow = qs + (rg * 16 + l16) * DQ + g;   // quad 4i + g: head-dim 16i + 4g .. +3
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < DQ / 4; ++i) {
+        const f32x4 qx = qrow[4 * i];
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qx[0], kx[i][0], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qx[1], kx[i][1], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qx[2], kx[i][2], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qx[3], kx[i][3], acc1, 0, 0, 0);
+      }
+      if (col < a.nb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[(rg * 16 + 4 * g + r) * a.nb + col] = orderable_key(acc0[r] + acc1[r]);
+      }
     }
   };
-  // two register buffers: the next block of this wave (every eighth) is
-  // loaded while this one's MFMAs run; the load after the last block
-  // repeats it, so that every iteration issues the same loads
   f32x4 kb0[DQ / 4], kb1[DQ / 4];
   const int last = nblk - 1;
   if (wave < nblk) {
     load_block(wave, kb0);
     for (int cb = wave;;) {
-      load_block(min(cb + kMfmaWaves, last), kb1);
+      load_block(min(cb + kWaves, last), kb1);
       score_block(cb, kb0);
-      cb += kMfmaWaves;
+      cb += kWaves;
       if (cb >= nblk) break;
-      load_block(min(cb + kMfmaWaves, last), kb0);
+      load_block(min(cb + kWaves, last), kb0);
       score_block(cb, kb1);
-      cb += kMfmaWaves;
+      cb += kWaves;
       if (cb >= nblk) break;
     }
   }
   __syncthreads();
   uint32_t* wh = hist + wave * 256;
-  for (int r = wave; r < nrows; r += kMfmaWaves)
+  for (int r = wave; r < nrows; r += kWaves)
     row_topk_regs<KPL>(sc + r * a.nb, a.nb, a.topk, wh, lane, sel + ((int64_t)bh * a.nq + row0 + r) * a.topk);
 }
 
 }  // namespace
 
+namespace {
+
+// LDS of the matrix-core kernel with RG groups of 16 rows: score rows,
+// per-wave histograms and qbar rows
+size_t mfma_lds_bytes(const VsaArgs& a, int rg) {
+  return (size_t)16 * rg * a.nb * 4 + (size_t)8 * rg * 256 * 4 + (size_t)16 * rg * a.D * 4;
+}
+
+// Row groups per workgroup: two when their LDS fits and the launch still
+// gives every CU a workgroup, else one.
+int mfma_row_groups(const VsaArgs& a) {
+  const int64_t wg2 = (int64_t)a.B * a.Hh * ((a.nq + 31) / 32);
+  return mfma_lds_bytes(a, 2) <= 160 * 1024 && wg2 >= 256 ? 2 : 1;
+}
+
+}  // namespace
+
 size_t vsa_select_lds_bytes(const VsaArgs& a) {
-  if (a.nb <= VSA_SELECT_MFMA_MAX_BLOCKS) return (size_t)kMfmaRows * a.nb * 4 + (size_t)kMfmaWaves * 256 * 4;
+  if (a.nb <= VSA_SELECT_MFMA_MAX_BLOCKS) return mfma_lds_bytes(a, mfma_row_groups(a));
   return (size_t)a.select_rows * a.D * 4 + (size_t)kColChunk * a.D * 4 + (size_t)kSelWaves * 256 * 4 +
          (size_t)a.select_rows * a.nb * 4;
 }
@@ -562,20 +579,27 @@ hipError_t launch_d(const VsaArgs& a, const float* qbar, const float* kbar, int3
   }
 }
 
-template <int D, int KPL>
+template <int D, int KPL, int RG>
 hipError_t launch_mfma_kpl(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel, size_t lds,
                            hipStream_t stream) {
   static std::atomic<uint64_t> raised{0};
   if (lds > 65536) {
     const hipError_t e =
-        vsa_raise_lds_limit(reinterpret_cast<const void*>(&vsa_score_topk_mfma_kernel<D, KPL>), raised);
+        vsa_raise_lds_limit(reinterpret_cast<const void*>(&vsa_score_topk_mfma_kernel<D, KPL, RG>), raised);
     if (e != hipSuccess) return e;
   }
-  const int groups = (a.nq + kMfmaRows - 1) / kMfmaRows;
+  const int groups = (a.nq + 16 * RG - 1) / (16 * RG);
   const int nwg = groups * a.B * a.Hh;
-  hipLaunchKernelGGL((vsa_score_topk_mfma_kernel<D, KPL>), dim3((nwg + 7) / 8 * 8), dim3(kMfmaWaves * 64), lds,
+  hipLaunchKernelGGL((vsa_score_topk_mfma_kernel<D, KPL, RG>), dim3((nwg + 7) / 8 * 8), dim3(RG * 8 * 64), lds,
                      stream, a, qbar, kbar, sel);
   return hipGetLastError();
+}
+
+template <int D, int KPL>
+hipError_t launch_mfma_rg(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel, size_t lds,
+                          hipStream_t stream) {
+  return mfma_row_groups(a) == 2 ? launch_mfma_kpl<D, KPL, 2>(a, qbar, kbar, sel, lds, stream)
+                                 : launch_mfma_kpl<D, KPL, 1>(a, qbar, kbar, sel, lds, stream);
 }
 
 // keys per lane of the register top-k: the next power of two >= nb / 64
@@ -583,11 +607,11 @@ template <int D>
 hipError_t launch_mfma(const VsaArgs& a, const float* qbar, const float* kbar, int32_t* sel, size_t lds,
                        hipStream_t stream) {
   const int kpl = (a.nb + 63) / 64;
-  if (kpl <= 2) return launch_mfma_kpl<D, 2>(a, qbar, kbar, sel, lds, stream);
-  if (kpl <= 4) return launch_mfma_kpl<D, 4>(a, qbar, kbar, sel, lds, stream);
-  if (kpl <= 8) return launch_mfma_kpl<D, 8>(a, qbar, kbar, sel, lds, stream);
-  if (kpl <= 16) return launch_mfma_kpl<D, 16>(a, qbar, kbar, sel, lds, stream);
-  return launch_mfma_kpl<D, 32>(a, qbar, kbar, sel, lds, stream);
+  if (kpl <= 2) return launch_mfma_rg<D, 2>(a, qbar, kbar, sel, lds, stream);
+  if (kpl <= 4) return launch_mfma_rg<D, 4>(a, qbar, kbar, sel, lds, stream);
+  if (kpl <= 8) return launch_mfma_rg<D, 8>(a, qbar, kbar, sel, lds, stream);
+  if (kpl <= 16) return launch_mfma_rg<D, 16>(a, qbar, kbar, sel, lds, stream);
+  return launch_mfma_rg<D, 32>(a, qbar, kbar, sel, lds, stream);
 }
 
 }  // namespace
