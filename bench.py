@@ -43,7 +43,8 @@ PEAK_MFMA_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": 2500.0}   # fp16 dense peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend.json")
 ATTEND_SOURCES = ["attend.hip", "vsa_device.h", "vsa_limits.h"]
-SUITE = (("wan_sweep", 16), ("wan_sweep", 32), ("wan_sweep", 120), ("long720p", None), ("prefix", None))
+SUITE = (("wan_sweep", 16), ("wan_sweep", 32), ("wan_sweep", 120), ("wan_whole", None), ("long720p", None),
+         ("prefix", None))
 
 
 def attend_source_hash() -> str:
@@ -245,6 +246,22 @@ def cache_bandwidth() -> dict:
     return json.loads(r.stdout)
 
 
+def step_probe() -> dict:
+    """Issue rates (cycles per iteration of exp2 / fma / MFMA mixes), LDS read
+    rates (bytes per clock per CU) and the MFMA-busy percentage of a synthetic
+    attention step with and without a barrier and copies: the in-tree probe
+    block_sparse_attention_raster_amd/step_probe (built with the library),
+    run as a child process."""
+    import subprocess
+    probe = os.path.join(ROOT, "block_sparse_attention_raster_amd", "step_probe")
+    if not os.path.exists(probe):
+        raise RuntimeError("step_probe is not built; run __graft_entry__.build() first")
+    r = subprocess.run([probe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError("step_probe failed:\n" + r.stderr)
+    return json.loads(r.stdout)
+
+
 def summarize_trace(path: str, skip: int, take: int = 0) -> str:
     """Per-kernel dispatch statistics of the library's kernels (vsa_*) in a
     rocprofv3 kernel-trace CSV, dropping the first ``skip`` dispatches of
@@ -295,6 +312,9 @@ def main(argv=None):
     ap.add_argument("--cache-bandwidth", action="store_true",
                     help="only measure read bandwidth from windows that fit the L2, the MALL or neither "
                          "(the rooflines of the small-cube attention)")
+    ap.add_argument("--step-probe", action="store_true",
+                    help="only measure issue and LDS rates and a synthetic attention step "
+                         "(what bounds the attention step's schedule)")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="only print per-kernel statistics of a rocprofv3 kernel-trace CSV")
     ap.add_argument("--skip", type=int, default=0, help="with --summarize-trace: warm-up dispatches to drop")
@@ -307,6 +327,9 @@ def main(argv=None):
         return 0
     if args.cache_bandwidth:
         print(json.dumps(cache_bandwidth()), flush=True)
+        return 0
+    if args.step_probe:
+        print(json.dumps(step_probe()), flush=True)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path shards over (batch, head) with no exchange "

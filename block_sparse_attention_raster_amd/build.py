@@ -1,5 +1,7 @@
 """Builds libvsa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and the
-benchmark's read-bandwidth probe (cache_probe).
+benchmark's two probes: read bandwidth per cache level (cache_probe) and the
+issue, LDS and synthetic-step rates that bound the attention step
+(step_probe).
 
     python -m block_sparse_attention_raster_amd.build
 """
@@ -17,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvsa.so")
 PROBE = os.path.join(PKG, "cache_probe")   # read-bandwidth probe of the benchmark
+STEP_PROBE = os.path.join(PKG, "step_probe")   # issue / LDS / synthetic-step probe of the benchmark
 BUILD_DIR = os.path.join(PKG, "_build")
 
 HIP_SOURCES = ["api.hip", "pool.hip", "select.hip", "attend.hip"]
@@ -66,9 +69,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
-    _run([hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", os.path.join(CSRC, "cache_probe.hip"), "-o", PROBE + ".tmp"])
-    os.replace(PROBE + ".tmp", PROBE)
+    probe_flags = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
+                   "-packed-fp32-ops"]
+    for src, out in (("cache_probe.hip", PROBE), ("step_probe.hip", STEP_PROBE)):
+        _run([hipcc, *probe_flags, os.path.join(CSRC, src), "-o", out + ".tmp"])
+        os.replace(out + ".tmp", out)
     return LIB
 
 

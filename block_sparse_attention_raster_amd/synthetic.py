@@ -65,6 +65,11 @@ WORKLOADS = {
         modification="cube_bias",
         note="Wan shape with a per-head, per-key-cube bias on K that makes "
              "cube scores peaked; top-k 16, 32 and 120 (all blocks)"),
+    "wan_whole": Workload(
+        "wan_whole", 2, 1, 24, 128, (32, 24, 40), (4, 8, 8), (64,),
+        note="Wan's heads, head dim, cube and keep on a (32, 24, 40) grid: "
+             "120 whole cubes of 256 tokens; times the attention without "
+             "partial query cubes"),
     "long720p": Workload(
         "long720p", 4, 1, 32, 128, (16, 46, 80), (4, 4, 4), (60,),
         note="58880 tokens, 960 cubes of up to 64 tokens, partial cubes "
