@@ -10,7 +10,8 @@
 //   - step: a synthetic attention step with the attention kernel's operand
 //     shapes (64-key tile, head dim 128, K read four slots ahead, V four
 //     slots ahead, the softmax's exp2 / pack / dot2 pipelined over the P.V
-//     slots) but no global memory, walker or masking, then with a barrier
+//     slots, P and the row sums used at the step's end as the row-sum check
+//     uses them) but no global memory, walker or masking, then with a barrier
 //     per two steps, with the step's global-to-LDS copies, and both; and the
 //     same step with 64 query rows per wave at one wave per SIMD.
 // Cycles come from s_memtime (the shader clock) per wave, median over waves.
@@ -265,14 +266,6 @@ __global__ void __launch_bounds__(NWAVE * 64) step_kernel(const float* __restric
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (it & 1) {
-      if constexpr (COPY) wait_vmcnt<4>();   // copies of the step before have landed
-      if constexpr (BAR) {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-      }
-    }
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       const int kk = NP - 1, pkb = kk / 8, phh = (kk % 8) / 4;
@@ -283,6 +276,21 @@ __global__ void __launch_bounds__(NWAVE * 64) step_kernel(const float* __restric
       for (int k2 = NP - 2; k2 < NP; ++k2)
         ps[b][k2 % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[b][k2]), one2, ps[b][k2 % 4],
                                                        false);
+    }
+    // the step's P and sums are used here, as the attention kernel's row-sum
+    // check uses them, so the compiler keeps the softmax inside the P.V slots
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      asm volatile("" ::"v"(pb[b][0][0]), "v"(pb[b][0][1]), "v"(pb[b][1][0]), "v"(pb[b][1][1]));
+      asm volatile("" ::"v"(ps[b][0]), "v"(ps[b][1]), "v"(ps[b][2]), "v"(ps[b][3]));
+    }
+    if (it & 1) {
+      if constexpr (COPY) wait_vmcnt<4>();   // copies of the step before have landed
+      if constexpr (BAR) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
     }
   }
   const long long t1 = clock64();
