@@ -300,6 +300,13 @@ def test_workload_wan():
     _full_check(w, 64, heads=[(0, 0), (0, 11), (0, 23)], blocks_per_head=6)
 
 
+def test_workload_wan_whole():
+    # the bench's whole-cube variant of the Wan shape: every query block a
+    # full 256-token cube, so every workgroup runs all eight waves
+    w = synthetic.WORKLOADS["wan_whole"]
+    _full_check(w, 64, heads=[(0, 0), (0, 13)], blocks_per_head=5)
+
+
 @pytest.mark.parametrize("topk", [16, 32, 120])
 def test_workload_wan_sweep(topk):
     w = synthetic.WORKLOADS["wan_sweep"]
