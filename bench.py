@@ -13,7 +13,9 @@ the GPU's own run), divided by the measured time. ``value`` and
 events on the stream the kernels run on split every step into pool, score +
 top-k and attention (median and mean over the steps). A second pass runs the
 same steps with the L2 and the MALL flushed before each (a 1 GiB buffer
-written outside the timed region), as between the layers of a real model.
+read outside the timed region, which leaves the caches holding clean lines
+of that buffer; a write would leave dirty lines whose write-back then lands
+inside the first kernel of the step), as between the layers of a real model.
 The roofline object is for the attention kernel (the dominant one). The
 other workloads of the suite (wan_sweep at top-k 16, 32 and 120, long720p,
 prefix) are timed in the same run and reported under ``suite``. The
@@ -186,16 +188,17 @@ class Run:
             ev[3].record()
 
     def timed(self, steps, flush=None):
-        """Events of `steps` steps; with `flush`, a buffer write before each
-        step, outside its events. Returns (per-step ms [steps, 4 phases:
-        pool, score, attend, call], wall ms of the loop)."""
+        """Events of `steps` steps; with `flush` (an int64 tensor), a read of
+        the whole buffer before each step, outside its events. Returns
+        (per-step ms [steps, 4 phases: pool, score, attend, call], wall ms of
+        the loop)."""
         torch = self.torch
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             if flush is not None:
-                flush.zero_()
+                flush.sum()
             self.step(events[i])
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3
@@ -305,7 +308,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-suite", action="store_true", help="time the headline workload only")
     ap.add_argument("--suite-steps", type=int, default=10)
-    ap.add_argument("--flush-mib", type=int, default=1024, help="buffer written before each flushed step")
+    ap.add_argument("--flush-mib", type=int, default=1024, help="buffer read before each flushed step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters)")
@@ -363,7 +366,7 @@ def main(argv=None):
     # the timed steps, back to back (the metric's wall clock), then the
     # same steps with the caches flushed before each
     ms, wall = run.timed(args.steps)
-    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+    flush = torch.zeros((args.flush_mib << 20) // 8, dtype=torch.int64, device=dev)
     ms_flushed, _ = run.timed(args.steps, flush=flush)
     del flush
     torch.cuda.empty_cache()
