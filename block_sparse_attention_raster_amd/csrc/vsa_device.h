@@ -73,8 +73,9 @@ struct VsaArgs {
   int32_t select_rows;   // query blocks per score/top-k workgroup
   int32_t tiles;         // query row tiles per query block
   int32_t f16;           // q, k, v, o are fp16 (else bf16)
-  int32_t walk_conc;     // attention workgroups resident per XCD whose walks
-                         // are phase-staggered (0: no stagger)
+  int32_t walk_conc;     // attention: period, in dispatch order within an
+                         // XCD, of the walks' staggered start positions
+                         // (about the resident workgroups; 0: no stagger)
   int32_t split_tail;    // attention: units at the end of each XCD's range
                          // that run as two half-row workgroups (0: none)
 };
